@@ -1,0 +1,206 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) MLA paged-decode library.
+ *
+ * The operation is DeepSeek-style Multi-Head Latent Attention decode in its
+ * absorbed ("data-movement friendly") form, as defined in the module
+ * docstring of vLLM's v1/attention/backends/mla/common.py, section
+ * "Data-Movement Friendly Approach": the query is absorbed through W_UK
+ * (ql_nope = q_nope . W_UK), every head attends over the same latent cache
+ * rows [kv_c | k_pe] (an MQA with QK head dim Lkv+R = 576 and V head dim
+ * Lkv = 512), and the latent output is up-projected through W_UV.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers unless the name ends in _host.
+ *    Tensors are caller-owned; run/absorb/up/merge allocate nothing.
+ *  - bf16 tensors are passed as raw 16-bit storage (void*), fp8 as bytes.
+ *  - Strides are in ELEMENTS of the tensor's own type.
+ *  - Every call is enqueued on the caller's HIP stream and returns without a
+ *    host synchronisation.  Device data (block_table entries, seq_lens) is a
+ *    precondition and is not read back: block_table[b][j] must be a valid page
+ *    in [0, num_pages) for every j < ceil(seq_lens[b] / page_size); entries
+ *    past that are never read (they may hold -1).
+ *  - Return value: MLA_OK or a negative mla_status.  Nothing throws or aborts
+ *    across the ABI.  mla_last_error() gives text for the calling thread's
+ *    last non-OK status.
+ *  - Dimensions supported: Lkv = 512 and R = 64 only (head size 576, the only
+ *    MLA head size the vLLM backends accept); 1 <= N <= 128 query heads;
+ *    1 <= Sq <= 8 query tokens per request, uniform over the batch (the ROCm
+ *    backend builds qo_indptr with a uniform query length); any page_size >= 1.
+ *    KV cache bf16 or OCP float8 e4m3fn; queries and latent output bf16;
+ *    LSE fp32, natural log, including the softmax scale.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* null pointer, bad size or stride, inconsistent arguments */
+  MLA_ERR_UNSUPPORTED = -2, /* valid request outside what the library implements     */
+  MLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the plan requires      */
+  MLA_ERR_HIP = -4,         /* a HIP runtime call failed; text from hipGetErrorString   */
+  MLA_ERR_INTERNAL = -5
+} mla_status;
+
+typedef enum { MLA_DT_BF16 = 0, MLA_DT_FP8_E4M3FN = 1, MLA_DT_FP32 = 2 } mla_dtype;
+
+/* Opaque, library-owned plan.  hipStream_t is passed as void* so that this
+ * header does not depend on the HIP headers. */
+typedef struct mla_plan_s* mla_plan;
+
+/*
+ * mla_decode_plan -- split-KV work plan for one batch (host work, once per
+ * batch, reused by every layer that decodes the same batch).
+ *
+ * The pages compute this schedule ahead of the forward pass and keep it off
+ * the per-layer path (rocm_aiter_mla, AiterMLAMetadataBuilder: persistent
+ * work / reduce maps filled per batch; mla/common.py metadata builder: avoid
+ * GPU-to-CPU syncs).  The rule is this library's own: the keys of all
+ * requests, in granules of 64, are dealt to at most num_cus / head_groups
+ * parts of near-equal cost; a request cut between parts is computed as
+ * partial states merged by LSE (the combiner of the mla/common.py docstring,
+ * "Chunked Prefill").  Rows of a request are Sq*N (row r = t*N + h); they are
+ * processed in head groups of up to 128 consecutive rows.
+ *
+ *  seq_lens_host      [B] host int32, keys per request (>= 0), including the
+ *                     Sq new tokens; query row t of a request sees keys
+ *                     j < seq_len - (Sq-1) + t (rocm_aiter_mla,
+ *                     AiterMLAImpl.forward_mqa, multi-token verify).
+ *  B, Sq, N, Lkv, R   batch, query tokens per request, heads, latent and rope width.
+ *  page_size          tokens per cache page (>= 1).
+ *  max_pages_per_req  columns of block_table; seq_len <= max_pages_per_req*page_size.
+ *  kv_dtype           MLA_DT_BF16 or MLA_DT_FP8_E4M3FN.
+ *  num_cus            compute units to plan for; <= 0 queries the current device.
+ *  stream             hipStream_t on which the plan's device upload is enqueued.
+ *  plan_out           receives the plan (owned by the library until mla_plan_destroy).
+ *  workspace_bytes_out  receives the workspace size mla_decode_run needs (0 if no
+ *                     request is split): fp32 partial outputs and LSE.
+ * Errors: INVALID_ARG (null pointers, B < 1, negative seq_len, seq_len beyond
+ * max_pages_per_req*page_size, page_size < 1), UNSUPPORTED (Lkv != 512,
+ * R != 64, N outside [1,128], Sq outside [1,8], other kv_dtype), HIP.
+ */
+int mla_decode_plan(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t N, int32_t Lkv,
+                    int32_t R, int32_t page_size, int32_t max_pages_per_req, int32_t kv_dtype,
+                    int32_t num_cus, void* stream, mla_plan* plan_out,
+                    size_t* workspace_bytes_out);
+
+/* Waits for the plan's stream, then frees the plan.  NULL is accepted. */
+int mla_plan_destroy(mla_plan plan);
+
+/*
+ * mla_decode_run -- latent attention of every query row over the paged cache.
+ *
+ * For request b, query row (t, h) and key j < n = max(0, L_b - (Sq-1) + t):
+ *   row_j = block_table[b][j / page_size] * page_size + j % page_size
+ *   s_j   = scale * kv_scale * (ql_nope[t,h] . kv_c[row_j] + q_pe[t,h] . k_pe[row_j])
+ *   o_latent[t,h] = kv_scale * sum_j softmax(s)_j kv_c[row_j]
+ *   lse[t,h]      = ln sum_j exp(s_j)
+ * (mla/common.py docstring, "Data-Movement Friendly Approach": SDPA of
+ * [ql_nope | q_pe] against [kv_c | k_pe] with value kv_c; the page expansion
+ * of rocm_aiter_mla, AiterMLAMetadataBuilder._build_decode.)  kv_scale is the
+ * per-tensor dequantisation scale of an fp8 cache (1 for bf16).  A row with
+ * n = 0 gets o_latent = 0 and lse = -inf.
+ *
+ *  q_nope    [B*Sq, N, 512] bf16, absorbed query ql_nope; token stride q_nope_s_tok, head stride q_nope_s_head.
+ *  q_pe      [B*Sq, N, 64] bf16, strides q_pe_s_tok, q_pe_s_head.
+ *  cache_kv_c / cache_k_pe  the latent cache [num_pages, page_size, 576] as two base
+ *            pointers sharing strides (canonical: cache_k_pe = cache_kv_c + 512 elements);
+ *            page stride cache_s_page, token stride cache_s_tok, dims contiguous.
+ *  block_table [B, max_pages_per_req] int32, row stride block_table_s_req.
+ *  seq_lens  [B] int32 device copy of the plan's seq_lens (must be equal).
+ *  o_latent  [B*Sq, N, 512] bf16 output, strides o_s_tok, o_s_head.
+ *  lse       [B*Sq, N] fp32 output (contiguous) or NULL.
+ *  workspace device scratch of at least the plan's workspace_bytes (may be NULL if 0).
+ * Errors: INVALID_ARG (nulls, bad strides, misaligned pointers: bf16 tensors need
+ * 16-byte aligned rows, fp8 8-byte), WORKSPACE, HIP.
+ */
+int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
+                   const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head,
+                   const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
+                   int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
+                   int64_t block_table_s_req, const int32_t* seq_lens, float scale,
+                   float kv_scale, void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_absorb_q -- ql_nope[t,h,l] = sum_p q_nope[t,h,p] * W_UK[l,h,p].
+ * mla/common.py docstring, "Data-Movement Friendly Approach" (einsum
+ * "snh,lnh->snl"); the layer runs it as a per-head bmm (N,B,P)x(N,P,L)
+ * (mla_attention, MLAAttention.forward_impl).  W_UK is the kv_b_proj slice
+ * [Lkv, N, P] (mla_attention, process_weights_after_loading).
+ *  q_nope [T, N, P] bf16 contiguous; W_UK [Lkv, N, P] bf16 contiguous;
+ *  ql_nope [T, N, Lkv] bf16 contiguous output.  fp32 accumulation, one
+ *  round-to-nearest-even to bf16.  P a multiple of 32 in [32, 256]; Lkv a multiple of 128.
+ */
+int mla_absorb_q(const void* q_nope, const void* W_UK, void* ql_nope, int32_t T, int32_t N,
+                 int32_t P, int32_t Lkv, void* stream);
+
+/*
+ * mla_up_v -- o[t,h,v] = sum_l o_latent[t,h,l] * W_UV[l,h,v].
+ * mla/common.py docstring, "Data-Movement Friendly Approach" (einsum
+ * "snl,lnv->snv"); mla_attention, _v_up_proj (bmm (N,B,L)x(N,L,V)).
+ *  o_latent [T, N, Lkv] bf16 contiguous; W_UV [Lkv, N, V] bf16 contiguous;
+ *  o [T, N, V] bf16 contiguous output.  V a multiple of 32 in [32, 256];
+ *  Lkv a multiple of 32.
+ */
+int mla_up_v(const void* o_latent, const void* W_UV, void* o, int32_t T, int32_t N, int32_t Lkv,
+             int32_t V, void* stream);
+
+/*
+ * merge_attn_states -- combine two attention states over disjoint key sets.
+ * mla/common.py docstring, "Chunked Prefill" (merge of prefix and suffix
+ * outputs with their LSE); argument order as the vLLM calls on the pages
+ * (output, output_lse, prefix_output, prefix_lse, suffix_output, suffix_lse).
+ *   m = max(lse_p, lse_s); w_x = exp(lse_x - m)
+ *   out = (w_p*prefix + w_s*suffix) / (w_p + w_s);  out_lse = m + ln(w_p + w_s)
+ * Both -inf: out = 0, out_lse = -inf.
+ *  out, prefix_o, suffix_o  [T, N, D] contiguous, element type o_dtype
+ *                           (MLA_DT_BF16 or MLA_DT_FP32); D a multiple of 8, <= 1024.
+ *  prefix_lse, suffix_lse   [T, N] fp32 natural-log; out_lse [T, N] fp32 or NULL.
+ */
+int merge_attn_states(void* out, float* out_lse, const void* prefix_o, const float* prefix_lse,
+                      const void* suffix_o, const float* suffix_lse, int32_t T, int32_t N,
+                      int32_t D, int32_t o_dtype, void* stream);
+
+/* Text of the calling thread's last non-OK status ("" if none). */
+const char* mla_last_error(void);
+
+/* ---- host-only and test exports (integer work, compared bit-exactly) ---- */
+
+/*
+ * mla_plan_compute_host -- the plan rule of mla_decode_plan on the host only
+ * (no HIP call).  Writes up to *n_items work items of 5 int32 each
+ * (part, request, kv_start, kv_end, partial slot or -1), ordered by part, and
+ * up to *n_reduce reduce entries of 3 int32 (request, first partial slot,
+ * count).  On return *n_items / *n_reduce hold the true counts; if a buffer
+ * is NULL or too small only the counts are returned.  *num_parts and
+ * *num_partials receive the part and partial-slot counts.
+ */
+int mla_plan_compute_host(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t N,
+                          int32_t num_cus, int32_t* work_host, int32_t* n_items,
+                          int32_t* reduce_host, int32_t* n_reduce, int32_t* num_parts,
+                          int32_t* num_partials);
+
+/* Copies a plan's work items and reduce entries (formats as above) to host memory. */
+int mla_plan_export(mla_plan plan, int32_t* work_host, int32_t* n_items, int32_t* reduce_host,
+                    int32_t* n_reduce);
+
+/*
+ * mla_debug_gather_rows -- the physical cache row the decode kernel computes for
+ * every key: rows_out[off_b + j] = block_table[b][j/page_size]*page_size + j%page_size
+ * for j < seq_lens[b], request-major (off_b = sum of earlier seq_lens).  Uses the
+ * plan's seq_lens and page_size.  rows_out: device int64 [sum seq_lens].
+ */
+int mla_debug_gather_rows(mla_plan plan, const int32_t* block_table, int64_t block_table_s_req,
+                          int64_t* rows_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_DECODE_H */

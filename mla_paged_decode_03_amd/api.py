@@ -1,0 +1,240 @@
+"""ctypes binding of libmla_decode.so: the C ABI of include/mla_decode.h, same names.
+
+Argument marshalling only: every step of the decode runs in the HIP library.
+torch supplies device memory and the current stream.  If the library has not
+been built this module raises on import, so no caller can fall back to
+anything else.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP, MLA_ERR_INTERNAL = \
+    0, -1, -2, -3, -4, -5
+MLA_DT_BF16, MLA_DT_FP8_E4M3FN, MLA_DT_FP32 = 0, 1, 2
+LKV, ROPE = 512, 64
+
+# torch first: it loads its own HIP runtime (SONAME libamdhip64.so.7), which the
+# library's dependency then resolves to, so the process holds exactly one runtime
+# and the library shares torch's devices, streams and allocations.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mla_paged_decode_03_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+_i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+_pi32, _pi64, _pf32 = C.POINTER(C.c_int32), C.POINTER(C.c_int64), C.POINTER(C.c_float)
+
+_SIGS = {
+    "mla_decode_plan": [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                        C.POINTER(_vp), C.POINTER(_sz)],
+    "mla_plan_destroy": [_vp],
+    "mla_decode_run": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i32, _vp, _i64,
+                       _vp, _f32, _f32, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mla_absorb_q": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp],
+    "mla_up_v": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp],
+    "merge_attn_states": [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp],
+    "mla_last_error": [],
+    "mla_plan_compute_host": [_pi32, _i32, _i32, _i32, _i32, _pi32, _pi32, _pi32, _pi32, _pi32, _pi32],
+    "mla_plan_export": [_vp, _pi32, _pi32, _pi32, _pi32],
+    "mla_debug_gather_rows": [_vp, _vp, _i64, _vp, _vp],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = C.c_char_p if _name == "mla_last_error" else C.c_int
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+def mla_last_error() -> str:
+    return _lib.mla_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != MLA_OK:
+        raise MLAError(rc, mla_last_error())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _host_i32(x) -> np.ndarray:
+    if hasattr(x, "cpu"):
+        x = x.cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+@dataclass
+class Plan:
+    handle: int
+    workspace_bytes: int
+    B: int
+    Sq: int
+    N: int
+    page_size: int
+    max_pages: int
+    kv_dtype: int
+
+    def destroy(self):
+        if self.handle:
+            _check(_lib.mla_plan_destroy(self.handle))
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            if self.handle:
+                _lib.mla_plan_destroy(self.handle)
+        except Exception:
+            pass
+
+
+def mla_decode_plan(seq_lens, Sq: int, N: int, page_size: int, max_pages_per_req: int,
+                    kv_dtype: int = MLA_DT_BF16, num_cus: int = 0, stream=None,
+                    Lkv: int = LKV, R: int = ROPE) -> Plan:
+    sl = _host_i32(seq_lens)
+    h = _vp()
+    ws = _sz()
+    _check(_lib.mla_decode_plan(sl.ctypes.data_as(_pi32), len(sl), Sq, N, Lkv, R, page_size,
+                                max_pages_per_req, kv_dtype, num_cus, _stream(stream),
+                                C.byref(h), C.byref(ws)))
+    return Plan(h.value, ws.value, len(sl), Sq, N, page_size, max_pages_per_req, kv_dtype)
+
+
+def mla_plan_destroy(plan: Plan):
+    plan.destroy()
+
+
+def _need(t, dtypes, name):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+
+
+def mla_decode_run(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale: float,
+                   kv_scale: float, o_latent, lse=None, workspace=None, stream=None,
+                   cache_k_pe=None):
+    """q_nope [T,N,512] bf16, q_pe [T,N,64] bf16, cache [pages, page_size, 576] (bf16 or fp8;
+    or the kv_c part when cache_k_pe is given), block_table [B, max_pages] int32,
+    seq_lens [B] int32 (device), o_latent [T,N,512] bf16, lse [T,N] fp32 or None."""
+    bf, f8 = torch.bfloat16, (torch.float8_e4m3fn, torch.uint8)
+    _need(q_nope, (bf,), "q_nope")
+    _need(q_pe, (bf,), "q_pe")
+    _need(cache, (bf,) if plan.kv_dtype == MLA_DT_BF16 else f8, "cache")
+    _need(block_table, (torch.int32,), "block_table")
+    _need(seq_lens, (torch.int32,), "seq_lens")
+    _need(o_latent, (bf,), "o_latent")
+    if lse is not None:
+        _need(lse, (torch.float32,), "lse")
+        if not lse.is_contiguous():
+            raise ValueError("lse must be contiguous [T, N]")
+    if q_nope.stride(2) != 1 or q_pe.stride(2) != 1 or o_latent.stride(2) != 1 or cache.stride(2) != 1:
+        raise ValueError("the last dimension of every tensor must be contiguous")
+    esz = cache.element_size()
+    kpe_ptr = cache.data_ptr() + LKV * esz if cache_k_pe is None else cache_k_pe.data_ptr()
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.mla_decode_run(
+        plan.handle, q_nope.data_ptr(), q_nope.stride(0), q_nope.stride(1),
+        q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1),
+        cache.data_ptr(), kpe_ptr, cache.stride(0), cache.stride(1), cache.shape[0],
+        block_table.data_ptr(), block_table.stride(0), seq_lens.data_ptr(),
+        float(scale), float(kv_scale), o_latent.data_ptr(), o_latent.stride(0), o_latent.stride(1),
+        _ptr(lse), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def _need_contig_bf16(*ts):
+    for t in ts:
+        _need(t, (torch.bfloat16,), "tensor")
+        if not t.is_contiguous():
+            raise ValueError("absorb / up-projection tensors must be contiguous")
+
+
+def mla_absorb_q(q_nope, W_UK, ql_nope, stream=None):
+    _need_contig_bf16(q_nope, W_UK, ql_nope)
+    T, N, P = q_nope.shape
+    Lkv = W_UK.shape[0]
+    _check(_lib.mla_absorb_q(q_nope.data_ptr(), W_UK.data_ptr(), ql_nope.data_ptr(), T, N, P, Lkv,
+                             _stream(stream)))
+
+
+def mla_up_v(o_latent, W_UV, o, stream=None):
+    _need_contig_bf16(o_latent, W_UV, o)
+    T, N, Lkv = o_latent.shape
+    V = W_UV.shape[2]
+    _check(_lib.mla_up_v(o_latent.data_ptr(), W_UV.data_ptr(), o.data_ptr(), T, N, Lkv, V,
+                         _stream(stream)))
+
+
+def merge_attn_states(out, out_lse, prefix_o, prefix_lse, suffix_o, suffix_lse, stream=None):
+    T, N, D = out.shape
+    for t in (out, prefix_o, suffix_o):
+        _need(t, (out.dtype,), "merge state")
+        if not t.is_contiguous():
+            raise ValueError("merge states must be contiguous [T, N, D]")
+    for t in (prefix_lse, suffix_lse) + ((out_lse,) if out_lse is not None else ()):
+        _need(t, (torch.float32,), "lse")
+    dt = MLA_DT_FP32 if out.dtype == torch.float32 else MLA_DT_BF16
+    _check(_lib.merge_attn_states(out.data_ptr(), _ptr(out_lse), prefix_o.data_ptr(),
+                                  prefix_lse.data_ptr(), suffix_o.data_ptr(), suffix_lse.data_ptr(),
+                                  T, N, D, dt, _stream(stream)))
+
+
+def mla_plan_compute_host(seq_lens, Sq: int, N: int, num_cus: int):
+    """Host-only plan rule: (work [n,5] int32, reduce [m,3] int32, num_parts, num_partials)."""
+    sl = _host_i32(seq_lens)
+    ni, nr, npart, npartial = _i32(0), _i32(0), _i32(0), _i32(0)
+    _check(_lib.mla_plan_compute_host(sl.ctypes.data_as(_pi32), len(sl), Sq, N, num_cus, None,
+                                      C.byref(ni), None, C.byref(nr), C.byref(npart), C.byref(npartial)))
+    work = np.zeros((max(ni.value, 1), 5), dtype=np.int32)
+    red = np.zeros((max(nr.value, 1), 3), dtype=np.int32)
+    _check(_lib.mla_plan_compute_host(sl.ctypes.data_as(_pi32), len(sl), Sq, N, num_cus,
+                                      work.ctypes.data_as(_pi32), C.byref(ni),
+                                      red.ctypes.data_as(_pi32), C.byref(nr), C.byref(npart),
+                                      C.byref(npartial)))
+    return work[:ni.value], red[:nr.value], npart.value, npartial.value
+
+
+def mla_plan_export(plan: Plan):
+    ni, nr = _i32(0), _i32(0)
+    _check(_lib.mla_plan_export(plan.handle, None, C.byref(ni), None, C.byref(nr)))
+    work = np.zeros((max(ni.value, 1), 5), dtype=np.int32)
+    red = np.zeros((max(nr.value, 1), 3), dtype=np.int32)
+    _check(_lib.mla_plan_export(plan.handle, work.ctypes.data_as(_pi32), C.byref(ni),
+                                red.ctypes.data_as(_pi32), C.byref(nr)))
+    return work[:ni.value], red[:nr.value]
+
+
+def mla_debug_gather_rows(plan: Plan, block_table, rows_out, stream=None):
+    _need(block_table, (torch.int32,), "block_table")
+    _need(rows_out, (torch.int64,), "rows_out")
+    _check(_lib.mla_debug_gather_rows(plan.handle, block_table.data_ptr(), block_table.stride(0),
+                                      rows_out.data_ptr(), _stream(stream)))
+
+
+def exported_symbols():
+    return list(_SIGS)

@@ -1,0 +1,368 @@
+// C ABI of the library: argument validation, plans, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mla_decode.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+struct mla_plan_s {
+  mla::Plan host;
+  int32_t Lkv = 0, R = 0, page_size = 0, max_pages = 0, kv_dtype = 0;
+  std::vector<int32_t> seq_lens;
+  int64_t total_keys = 0;
+  size_t ws_bytes = 0;
+  hipStream_t stream = nullptr;
+  int device = 0;
+  int32_t* d_buf = nullptr;  // segs | part_begin | reduce | seq_lens | pad | offsets (int64)
+  int32_t* h_buf = nullptr;  // pinned staging of the same words
+  size_t words = 0;
+  size_t off_part = 0, off_reduce = 0, off_seq = 0, off_offsets = 0;
+};
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_err.c_str(); }
+
+static int validate_dims(int32_t B, int32_t Sq, int32_t N, int32_t Lkv, int32_t R, int32_t page_size,
+                         int32_t max_pages, int32_t kv_dtype) {
+  if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B must be >= 1");
+  if (page_size < 1) return fail(MLA_ERR_INVALID_ARG, "page_size must be >= 1");
+  if (max_pages < 1) return fail(MLA_ERR_INVALID_ARG, "max_pages_per_req must be >= 1");
+  if (Lkv != mla::kLkv || R != mla::kRope)
+    return fail(MLA_ERR_UNSUPPORTED, "only Lkv = 512 and R = 64 (head size 576) are supported");
+  if (N < 1 || N > 128) return fail(MLA_ERR_UNSUPPORTED, "N must be in [1, 128]");
+  if (Sq < 1 || Sq > 8) return fail(MLA_ERR_UNSUPPORTED, "Sq must be in [1, 8]");
+  if (kv_dtype != MLA_DT_BF16 && kv_dtype != MLA_DT_FP8_E4M3FN)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_dtype must be MLA_DT_BF16 or MLA_DT_FP8_E4M3FN");
+  return MLA_OK;
+}
+
+int mla_plan_compute_host(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t N,
+                          int32_t num_cus, int32_t* work_host, int32_t* n_items,
+                          int32_t* reduce_host, int32_t* n_reduce, int32_t* num_parts,
+                          int32_t* num_partials) {
+  if (!seq_lens_host || !n_items || !n_reduce) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || Sq < 1 || N < 1 || num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  mla::Plan p;
+  std::string err;
+  if (!mla::build_plan(seq_lens_host, B, Sq, N, num_cus, &p, &err)) return fail(MLA_ERR_INVALID_ARG, err);
+  const int32_t ni = (int32_t)p.segs.size(), nr = (int32_t)p.reduce.size() / 3;
+  if (work_host && *n_items >= ni) {
+    for (int32_t pt = 0; pt < p.num_parts; ++pt)
+      for (int32_t s = p.part_begin[pt]; s < p.part_begin[pt + 1]; ++s) {
+        int32_t* o = work_host + 5 * s;
+        o[0] = pt;
+        o[1] = p.segs[s].req;
+        o[2] = p.segs[s].kv_start;
+        o[3] = p.segs[s].kv_end;
+        o[4] = p.segs[s].partial;
+      }
+  }
+  if (reduce_host && *n_reduce >= nr) std::memcpy(reduce_host, p.reduce.data(), sizeof(int32_t) * 3 * nr);
+  *n_items = ni;
+  *n_reduce = nr;
+  if (num_parts) *num_parts = p.num_parts;
+  if (num_partials) *num_partials = p.num_partials;
+  return MLA_OK;
+}
+
+int mla_decode_plan(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t N, int32_t Lkv,
+                    int32_t R, int32_t page_size, int32_t max_pages_per_req, int32_t kv_dtype,
+                    int32_t num_cus, void* stream, mla_plan* plan_out,
+                    size_t* workspace_bytes_out) {
+  if (!seq_lens_host || !plan_out || !workspace_bytes_out) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  *plan_out = nullptr;
+  int rc = validate_dims(B, Sq, N, Lkv, R, page_size, max_pages_per_req, kv_dtype);
+  if (rc) return rc;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "negative seq_len");
+    if ((int64_t)seq_lens_host[b] > (int64_t)max_pages_per_req * page_size)
+      return fail(MLA_ERR_INVALID_ARG, "seq_len exceeds max_pages_per_req * page_size");
+  }
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (num_cus <= 0) {
+    e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  auto* p = new mla_plan_s();
+  std::string err;
+  if (!mla::build_plan(seq_lens_host, B, Sq, N, num_cus, &p->host, &err)) {
+    delete p;
+    return fail(MLA_ERR_INTERNAL, err);
+  }
+  p->Lkv = Lkv;
+  p->R = R;
+  p->page_size = page_size;
+  p->max_pages = max_pages_per_req;
+  p->kv_dtype = kv_dtype;
+  p->seq_lens.assign(seq_lens_host, seq_lens_host + B);
+  p->stream = (hipStream_t)stream;
+  p->device = device;
+  p->ws_bytes = (size_t)p->host.num_partials * Sq * N * (mla::kLkv * 4 + 4);
+
+  const size_t nseg = p->host.segs.size();
+  p->off_part = 4 * nseg;
+  p->off_reduce = p->off_part + p->host.part_begin.size();
+  p->off_seq = p->off_reduce + p->host.reduce.size();
+  p->off_offsets = (p->off_seq + B + 1) & ~(size_t)1;
+  p->words = p->off_offsets + 2 * (size_t)B;
+  std::vector<int32_t> w(p->words, 0);
+  for (size_t s = 0; s < nseg; ++s) {
+    const auto& sg = p->host.segs[s];
+    w[4 * s] = sg.req;
+    w[4 * s + 1] = sg.kv_start;
+    w[4 * s + 2] = sg.kv_end;
+    w[4 * s + 3] = sg.partial;
+  }
+  std::memcpy(&w[p->off_part], p->host.part_begin.data(), 4 * p->host.part_begin.size());
+  if (!p->host.reduce.empty()) std::memcpy(&w[p->off_reduce], p->host.reduce.data(), 4 * p->host.reduce.size());
+  std::memcpy(&w[p->off_seq], seq_lens_host, 4 * (size_t)B);
+  int64_t acc = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    std::memcpy(&w[p->off_offsets + 2 * b], &acc, 8);
+    acc += seq_lens_host[b];
+  }
+  p->total_keys = acc;
+
+  e = hipMalloc((void**)&p->d_buf, 4 * p->words);
+  if (e == hipSuccess) e = hipHostMalloc((void**)&p->h_buf, 4 * p->words, hipHostMallocDefault);
+  if (e == hipSuccess) {
+    std::memcpy(p->h_buf, w.data(), 4 * p->words);
+    e = hipMemcpyAsync(p->d_buf, p->h_buf, 4 * p->words, hipMemcpyHostToDevice, p->stream);
+  }
+  if (e != hipSuccess) {
+    if (p->d_buf) (void)hipFree(p->d_buf);
+    if (p->h_buf) (void)hipHostFree(p->h_buf);
+    delete p;
+    return hip_fail(e, "plan upload");
+  }
+  *plan_out = p;
+  *workspace_bytes_out = p->ws_bytes;
+  return MLA_OK;
+}
+
+int mla_plan_destroy(mla_plan plan) {
+  if (!plan) return MLA_OK;
+  hipError_t e = hipStreamSynchronize(plan->stream);
+  hipError_t e2 = hipFree(plan->d_buf);
+  hipError_t e3 = hipHostFree(plan->h_buf);
+  delete plan;
+  if (e != hipSuccess) return hip_fail(e, "mla_plan_destroy: stream sync");
+  if (e2 != hipSuccess) return hip_fail(e2, "mla_plan_destroy: hipFree");
+  if (e3 != hipSuccess) return hip_fail(e3, "mla_plan_destroy: hipHostFree");
+  return MLA_OK;
+}
+
+int mla_plan_export(mla_plan plan, int32_t* work_host, int32_t* n_items, int32_t* reduce_host,
+                    int32_t* n_reduce) {
+  if (!plan || !n_items || !n_reduce) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  const auto& p = plan->host;
+  const int32_t ni = (int32_t)p.segs.size(), nr = (int32_t)p.reduce.size() / 3;
+  if (work_host && *n_items >= ni) {
+    for (int32_t pt = 0; pt < p.num_parts; ++pt)
+      for (int32_t s = p.part_begin[pt]; s < p.part_begin[pt + 1]; ++s) {
+        int32_t* o = work_host + 5 * s;
+        o[0] = pt;
+        o[1] = p.segs[s].req;
+        o[2] = p.segs[s].kv_start;
+        o[3] = p.segs[s].kv_end;
+        o[4] = p.segs[s].partial;
+      }
+  }
+  if (reduce_host && *n_reduce >= nr) std::memcpy(reduce_host, p.reduce.data(), sizeof(int32_t) * 3 * nr);
+  *n_items = ni;
+  *n_reduce = nr;
+  return MLA_OK;
+}
+
+int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
+                   const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head,
+                   const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
+                   int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
+                   int64_t block_table_s_req, const int32_t* seq_lens, float scale,
+                   float kv_scale, void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARG, "null plan");
+  if (!q_nope || !q_pe || !cache_kv_c || !cache_k_pe || !block_table || !seq_lens || !o_latent)
+    return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+  const auto& hp = plan->host;
+  if (q_nope_s_tok < 1 || q_nope_s_head < 1 || q_pe_s_tok < 1 || q_pe_s_head < 1 || o_s_tok < 1 ||
+      o_s_head < 1 || cache_s_page < 1 || cache_s_tok < 1 || block_table_s_req < plan->max_pages)
+    return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if (!std::isfinite(scale) || !std::isfinite(kv_scale) || kv_scale <= 0.f)
+    return fail(MLA_ERR_INVALID_ARG, "scale and kv_scale must be finite, kv_scale > 0");
+  // 16-byte vector loads of 8 bf16 (8 fp8 bytes for the cache), 8-byte output stores.
+  const bool fp8 = plan->kv_dtype == MLA_DT_FP8_E4M3FN;
+  const size_t cal = fp8 ? 8 : 16;
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || q_nope_s_tok % 8 || q_nope_s_head % 8 ||
+      q_pe_s_tok % 8 || q_pe_s_head % 8)
+    return fail(MLA_ERR_INVALID_ARG, "queries need 16-byte aligned rows (pointer and strides)");
+  if (!aligned(cache_kv_c, cal) || !aligned(cache_k_pe, cal) || cache_s_page % 8 || cache_s_tok % 8)
+    return fail(MLA_ERR_INVALID_ARG, "cache rows must be aligned to 8 elements");
+  if (!aligned(o_latent, 8) || o_s_tok % 4 || o_s_head % 4)
+    return fail(MLA_ERR_INVALID_ARG, "o_latent needs 8-byte aligned rows");
+  if (plan->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+      return fail(MLA_ERR_WORKSPACE, "workspace smaller than the plan requires (" +
+                                         std::to_string(plan->ws_bytes) + " bytes)");
+    if (!aligned(workspace, 16)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device) return fail(MLA_ERR_INVALID_ARG, "plan was made for another device");
+
+  mla::DecodeArgs a{};
+  a.q_nope = (const uint16_t*)q_nope;
+  a.q_nope_s_tok = q_nope_s_tok;
+  a.q_nope_s_head = q_nope_s_head;
+  a.q_pe = (const uint16_t*)q_pe;
+  a.q_pe_s_tok = q_pe_s_tok;
+  a.q_pe_s_head = q_pe_s_head;
+  a.kv_c = cache_kv_c;
+  a.k_pe = cache_k_pe;
+  a.s_page = cache_s_page;
+  a.s_tok = cache_s_tok;
+  a.block_table = block_table;
+  a.bt_s = block_table_s_req;
+  a.seq_lens = seq_lens;
+  a.segs = plan->d_buf;
+  a.part_begin = plan->d_buf + plan->off_part;
+  a.o = (uint16_t*)o_latent;
+  a.o_s_tok = o_s_tok;
+  a.o_s_head = o_s_head;
+  a.lse = lse;
+  const size_t R = (size_t)hp.Sq * hp.N;
+  a.ws_o = (float*)workspace;
+  a.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * R * mla::kLkv * 4) : nullptr;
+  a.qk_scale_log2 = scale * kv_scale * 1.4426950408889634f;
+  a.out_scale = kv_scale;
+  a.Sq = hp.Sq;
+  a.N = hp.N;
+  a.page_size = plan->page_size;
+  a.num_parts = hp.num_parts;
+  a.head_groups = hp.head_groups;
+  hipStream_t s = (hipStream_t)stream;
+  e = mla::launch_decode(a, fp8, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  mla::MergeArgs m{};
+  m.reduce = plan->d_buf + plan->off_reduce;
+  m.n_reduce = (int32_t)hp.reduce.size() / 3;
+  m.ws_o = a.ws_o;
+  m.ws_lse = a.ws_lse;
+  m.o = a.o;
+  m.o_s_tok = o_s_tok;
+  m.o_s_head = o_s_head;
+  m.lse = lse;
+  m.Sq = hp.Sq;
+  m.N = hp.N;
+  e = mla::launch_split_merge(m, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return MLA_OK;
+}
+
+int mla_absorb_q(const void* q_nope, const void* W_UK, void* ql_nope, int32_t T, int32_t N,
+                 int32_t P, int32_t Lkv, void* stream) {
+  if (!q_nope || !W_UK || !ql_nope) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (T < 0 || N < 1 || P < 8 || Lkv < 8) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (P % 8 || Lkv % 8) return fail(MLA_ERR_UNSUPPORTED, "P and Lkv must be multiples of 8");
+  if (!aligned(q_nope, 16) || !aligned(W_UK, 16) || !aligned(ql_nope, 16))
+    return fail(MLA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  mla::GemmArgs g{};
+  g.A = (const uint16_t*)q_nope;  // (h, m=t, k=p) at t*N*P + h*P + p
+  g.a_sh = P;
+  g.a_sm = (int64_t)N * P;
+  g.B = (const uint16_t*)W_UK;  // (h, n=l, k=p) at l*N*P + h*P + p
+  g.b_sh = P;
+  g.b_sn = (int64_t)N * P;
+  g.b_sk = 1;
+  g.C = (uint16_t*)ql_nope;  // (h, t, l) at t*N*Lkv + h*Lkv + l
+  g.c_sh = Lkv;
+  g.c_sm = (int64_t)N * Lkv;
+  g.H = N;
+  g.M = T;
+  g.Nn = Lkv;
+  g.K = P;
+  hipError_t e = mla::launch_gemm(g, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "absorb launch");
+}
+
+int mla_up_v(const void* o_latent, const void* W_UV, void* o, int32_t T, int32_t N, int32_t Lkv,
+             int32_t V, void* stream) {
+  if (!o_latent || !W_UV || !o) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (T < 0 || N < 1 || V < 8 || Lkv < 8) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (V % 8 || Lkv % 8) return fail(MLA_ERR_UNSUPPORTED, "V and Lkv must be multiples of 8");
+  if (!aligned(o_latent, 16) || !aligned(W_UV, 16) || !aligned(o, 16))
+    return fail(MLA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  mla::GemmArgs g{};
+  g.A = (const uint16_t*)o_latent;  // (h, t, k=l) at t*N*Lkv + h*Lkv + l
+  g.a_sh = Lkv;
+  g.a_sm = (int64_t)N * Lkv;
+  g.B = (const uint16_t*)W_UV;  // (h, n=v, k=l) at l*N*V + h*V + v
+  g.b_sh = V;
+  g.b_sn = 1;
+  g.b_sk = (int64_t)N * V;
+  g.C = (uint16_t*)o;  // (h, t, v) at t*N*V + h*V + v
+  g.c_sh = V;
+  g.c_sm = (int64_t)N * V;
+  g.H = N;
+  g.M = T;
+  g.Nn = V;
+  g.K = Lkv;
+  hipError_t e = mla::launch_gemm(g, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "up-projection launch");
+}
+
+int merge_attn_states(void* out, float* out_lse, const void* prefix_o, const float* prefix_lse,
+                      const void* suffix_o, const float* suffix_lse, int32_t T, int32_t N,
+                      int32_t D, int32_t o_dtype, void* stream) {
+  if (!out || !prefix_o || !prefix_lse || !suffix_o || !suffix_lse)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (T < 0 || N < 1 || D < 8) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (D % 8) return fail(MLA_ERR_UNSUPPORTED, "D must be a multiple of 8");
+  if (o_dtype != MLA_DT_BF16 && o_dtype != MLA_DT_FP32)
+    return fail(MLA_ERR_UNSUPPORTED, "o_dtype must be MLA_DT_BF16 or MLA_DT_FP32");
+  if (!aligned(out, 16) || !aligned(prefix_o, 16) || !aligned(suffix_o, 16))
+    return fail(MLA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  hipError_t e = mla::launch_merge_two(out, out_lse, prefix_o, prefix_lse, suffix_o, suffix_lse,
+                                       (int64_t)T * N, D, o_dtype == MLA_DT_FP32, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "merge launch");
+}
+
+int mla_debug_gather_rows(mla_plan plan, const int32_t* block_table, int64_t block_table_s_req,
+                          int64_t* rows_out, void* stream) {
+  if (!plan || !block_table || !rows_out) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (block_table_s_req < plan->max_pages) return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  hipError_t e = mla::launch_gather_rows(block_table, block_table_s_req, plan->d_buf + plan->off_seq,
+                                         (const int64_t*)(plan->d_buf + plan->off_offsets), plan->host.B,
+                                         plan->page_size, rows_out, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "gather-rows launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Shared device helpers for the gfx950 kernels (wave64, MFMA, bf16/fp8).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+// D += A * B on a 32x32x16 bf16 tile.  Lane l holds A[l%32][8*(l/32)+e] and
+// B[8*(l/32)+e][l%32] (e = 0..7); D[i][j] lives in lane j + 32*((i/4)%2),
+// element 4*(i/8) + i%4.
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Round-to-nearest-even float -> bf16 pattern (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)bf16_rne(lo) | ((uint32_t)bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Four OCP e4m3fn bytes -> four bf16 values (two dwords).  Every e4m3fn value
+// is exactly representable in bf16, so the float -> bf16 step is a truncation.
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
+  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  u32x2_t r;
+  r[0] = (f32_bits(lo[0]) >> 16) | (f32_bits(lo[1]) & 0xFFFF0000u);
+  r[1] = (f32_bits(hi[0]) >> 16) | (f32_bits(hi[1]) & 0xFFFF0000u);
+  return r;
+}
+
+// Load through the constant address space: with a wave-uniform address this
+// becomes a scalar (SMEM) load instead of a vector load.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace mla

@@ -1,0 +1,121 @@
+// Per-head batched bf16 GEMM on MFMA for the W_UK absorption and the W_UV
+// up-projection (vLLM mla/common.py module docstring, "Data-Movement Friendly
+// Approach": ql_nope = einsum("snh,lnh->snl", q_nope, W_UK) and
+// o = einsum("snl,lnv->snv", o_latent, W_UV); the layer runs both as bmm over
+// heads).
+//
+//   C[h][m][n] = sum_k A[h][m][k] * B[h][n][k]
+//
+// One workgroup (4 waves) computes a 64 (m) x 128 (n) tile of one head and
+// walks K in chunks of 64 staged through LDS.  The MFMA computes the tile
+// transposed (rows = n, columns = m) so that each lane ends up with 4
+// consecutive n of one m, which it stores as 8 bytes.  B is either
+// k-contiguous (W_UK: [Lkv][N][P], k = p) or n-contiguous (W_UV: [Lkv][N][V],
+// k = l); the latter is transposed 8x8 in registers on its way into LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kBM = 64, kBN = 128, kBK = 64;
+
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // [row][8 chunks of 16 B]
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+template <bool B_NCONTIG>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) char sa[kBM * kBK * 2];
+  __shared__ __attribute__((aligned(16))) char sb[kBN * kBK * 2];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l32 = l & 31, hh = l >> 5;
+  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM, h = blockIdx.z;
+  const uint16_t* A = g.A + (int64_t)h * g.a_sh;
+  const uint16_t* B = g.B + (int64_t)h * g.b_sh;
+  f32x16_t acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+
+  for (int k0 = 0; k0 < g.K; k0 += kBK) {
+    // A tile: 64 rows x 8 chunks
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i, m = u >> 3, c = u & 7;
+      u32x4_t v = u32x4_t{0, 0, 0, 0};
+      if (m0 + m < g.M && k0 + 8 * c < g.K) v = *(const u32x4_t*)(A + (int64_t)(m0 + m) * g.a_sm + k0 + 8 * c);
+      *(u32x4_t*)(sa + tile_off(m, c)) = v;
+    }
+    if constexpr (!B_NCONTIG) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int u = tid + 256 * i, n = u >> 3, c = u & 7;
+        u32x4_t v = u32x4_t{0, 0, 0, 0};
+        if (n0 + n < g.Nn && k0 + 8 * c < g.K)
+          v = *(const u32x4_t*)(B + (int64_t)(n0 + n) * g.b_sn + k0 + 8 * c);
+        *(u32x4_t*)(sb + tile_off(n, c)) = v;
+      }
+    } else if (tid < 128) {
+      const int ko = tid >> 4, no = tid & 15;
+      u32x4_t r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + 8 * ko + e;
+        r[e] = u32x4_t{0, 0, 0, 0};
+        if (k < g.K && n0 + 8 * no < g.Nn) r[e] = *(const u32x4_t*)(B + (int64_t)k * g.b_sk + n0 + 8 * no);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32x4_t o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t x = r[2 * k][c >> 1], y = r[2 * k + 1][c >> 1];
+          o[k] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+        }
+        *(u32x4_t*)(sb + tile_off(8 * no + c, ko)) = o;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const u32x4_t af = *(const u32x4_t*)(sb + tile_off(32 * w + l32, 2 * ks + hh));
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4_t bf = *(const u32x4_t*)(sa + tile_off(32 * mb + l32, 2 * ks + hh));
+        acc[mb] = mfma32(af, bf, acc[mb]);
+      }
+    }
+    __syncthreads();
+  }
+  uint16_t* C = g.C + (int64_t)h * g.c_sh;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = m0 + 32 * mb + l32;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int n = n0 + 32 * w + 8 * gq + 4 * hh;
+      if (n >= g.Nn) continue;
+      u32x2_t pk;
+      pk[0] = pack_bf16x2(acc[mb][4 * gq], acc[mb][4 * gq + 1]);
+      pk[1] = pack_bf16x2(acc[mb][4 * gq + 2], acc[mb][4 * gq + 3]);
+      *(u32x2_t*)(C + (int64_t)m * g.c_sm + n) = pk;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
+  if (g.M == 0 || g.H == 0) return hipSuccess;
+  const dim3 grid((g.Nn + kBN - 1) / kBN, (g.M + kBM - 1) / kBM, g.H), block(256);
+  if (g.b_sk == 1)
+    hipLaunchKernelGGL(gemm_kernel<false>, grid, block, 0, stream, g);
+  else
+    hipLaunchKernelGGL(gemm_kernel<true>, grid, block, 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,67 @@
+// Kernel argument blocks and launchers (host <-> device interface inside the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace mla {
+
+struct DecodeArgs {
+  const uint16_t* q_nope;  // [T, N, 512] bf16
+  int64_t q_nope_s_tok, q_nope_s_head;
+  const uint16_t* q_pe;    // [T, N, 64] bf16
+  int64_t q_pe_s_tok, q_pe_s_head;
+  const void* kv_c;        // cache base for columns 0..511 (bf16 or e4m3fn)
+  const void* k_pe;        // cache base for columns 512..575
+  int64_t s_page, s_tok;   // cache strides in elements
+  const int32_t* block_table;
+  int64_t bt_s;
+  const int32_t* seq_lens;
+  const int32_t* part_begin;  // [num_parts + 1]
+  const int32_t* segs;        // [num_segs][4]: req, kv_start, kv_end, partial
+  uint16_t* o;                // [T, N, 512] bf16
+  int64_t o_s_tok, o_s_head;
+  float* lse;                 // [T, N] or null
+  float* ws_o;                // [partials, Sq*N, 512]
+  float* ws_lse;              // [partials, Sq*N]
+  float qk_scale_log2;        // scale * kv_scale * log2(e)
+  float out_scale;            // kv_scale
+  int32_t Sq, N, page_size, num_parts, head_groups;
+};
+
+struct MergeArgs {
+  const int32_t* reduce;  // [n_reduce][3]: req, first partial, count
+  int32_t n_reduce;
+  const float* ws_o;
+  const float* ws_lse;
+  uint16_t* o;
+  int64_t o_s_tok, o_s_head;
+  float* lse;
+  int32_t Sq, N;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_split_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_merge_two(void* out, float* out_lse, const void* prefix_o, const float* prefix_lse,
+                            const void* suffix_o, const float* suffix_lse, int64_t rows, int32_t D,
+                            bool fp32, hipStream_t stream);
+// C[h][m][n] = sum_k A[h][m][k] * B[h][n][k] in bf16 with fp32 accumulation.
+// A: element (h,m,k) at h*a_sh + m*a_sm + k.  B: (h,n,k) at h*b_sh + n*b_sn + k*b_sk,
+// with either b_sk == 1 (k-contiguous) or b_sn == 1 (n-contiguous).
+// C: (h,m,n) at h*c_sh + m*c_sm + n.
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t a_sh, a_sm;
+  const uint16_t* B;
+  int64_t b_sh, b_sn, b_sk;
+  uint16_t* C;
+  int64_t c_sh, c_sm;
+  int32_t H, M, Nn, K;
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gather_rows(const int32_t* block_table, int64_t bt_s, const int32_t* seq_lens,
+                              const int64_t* offsets, int32_t B, int32_t page_size, int64_t* rows,
+                              hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,150 @@
+// LSE merge of partial attention states (split-KV reduce and merge_attn_states).
+//
+// For states (o_i, lse_i) over disjoint key sets (vLLM mla/common.py module
+// docstring, "Chunked Prefill": merge_attn_states of prefix and suffix):
+//   m = max lse_i, w_i = exp(lse_i - m), o = sum w_i o_i / sum w_i,
+//   lse = m + ln sum w_i;  all -inf -> o = 0, lse = -inf.
+// One wave merges one row; each lane owns 8 consecutive columns per step.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+__global__ __launch_bounds__(256) void split_merge_kernel(MergeArgs a) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int R = a.Sq * a.N;
+  const int red = blockIdx.x;
+  const int r = blockIdx.y * 4 + w;
+  if (red >= a.n_reduce || r >= R) return;
+  const int b = a.reduce[3 * red], base = a.reduce[3 * red + 1], n = a.reduce[3 * red + 2];
+  // Every lane derives the weights itself (n <= 64 broadcast loads): no LDS, no barrier.
+  const float* lse_i = a.ws_lse + (int64_t)base * R + r;
+  float m = -INFINITY;
+  for (int i = 0; i < n; ++i) m = fmaxf(m, lse_i[(int64_t)i * R]);
+  const bool dead = (m == -INFINITY);
+  float z = 0.f;
+  if (!dead)
+    for (int i = 0; i < n; ++i) z += fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e);
+  const float inv = dead ? 0.f : 1.f / z;
+  const int col = 8 * l;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  if (!dead) {
+    for (int i = 0; i < n; ++i) {
+      const float wi = fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e) * inv;
+      const float* src = a.ws_o + ((int64_t)(base + i) * R + r) * kLkv + col;
+      const f32x4_t x0 = *(const f32x4_t*)src;
+      const f32x4_t x1 = *(const f32x4_t*)(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += wi * x0[e];
+        acc[4 + e] += wi * x1[e];
+      }
+    }
+  }
+  const int t = r / a.N, h = r - t * a.N;
+  const int64_t tok = (int64_t)b * a.Sq + t;
+  uint16_t* dst = a.o + tok * a.o_s_tok + (int64_t)h * a.o_s_head + col;
+  *(u32x4_t*)dst = u32x4_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                           pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  if (a.lse && l == 0) a.lse[tok * a.N + h] = dead ? -INFINITY : m + fast_log2(z) * kLn2;
+}
+
+__device__ __forceinline__ void load8(const void* p, bool fp32, float* x) {
+  if (fp32) {
+    const f32x4_t a = *(const f32x4_t*)p;
+    const f32x4_t b = *((const f32x4_t*)p + 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[4 + e] = b[e];
+    }
+  } else {
+    const u32x4_t v = *(const u32x4_t*)p;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_to_f32((uint16_t)(v[k] & 0xFFFF));
+      x[2 * k + 1] = bf16_to_f32((uint16_t)(v[k] >> 16));
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void merge_two_kernel(void* out, float* out_lse, const void* po,
+                                                        const float* plse, const void* so,
+                                                        const float* slse, int64_t rows, int D,
+                                                        int fp32) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + w;
+  if (r >= rows) return;
+  const float lp = plse[r], ls = slse[r];
+  const float m = fmaxf(lp, ls);
+  float wp = 0.f, wsf = 0.f, lse = -INFINITY;
+  if (m != -INFINITY) {
+    wp = fast_exp2((lp - m) * kLog2e);
+    wsf = fast_exp2((ls - m) * kLog2e);
+    const float z = wp + wsf;
+    lse = m + fast_log2(z) * kLn2;
+    wp /= z;
+    wsf /= z;
+  }
+  const int esz = fp32 ? 4 : 2;
+  for (int c = 8 * l; c < D; c += 512) {
+    float x[8], y[8];
+    const int64_t off = (r * D + c) * esz;
+    load8((const char*)po + off, fp32, x);
+    load8((const char*)so + off, fp32, y);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = wp * x[e] + wsf * y[e];
+    if (fp32) {
+      *(f32x4_t*)((char*)out + off) = f32x4_t{o[0], o[1], o[2], o[3]};
+      *((f32x4_t*)((char*)out + off) + 1) = f32x4_t{o[4], o[5], o[6], o[7]};
+    } else {
+      *(u32x4_t*)((char*)out + off) = u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                              pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+    }
+  }
+  if (out_lse && l == 0) out_lse[r] = lse;
+}
+
+__global__ void gather_rows_kernel(const int32_t* bt, int64_t bt_s, const int32_t* seq_lens,
+                                   const int64_t* offsets, int page_size, int64_t* rows) {
+  const int b = blockIdx.x;
+  const int L = seq_lens[b];
+  const int32_t* row = bt + (int64_t)b * bt_s;
+  for (int j = threadIdx.x; j < L; j += blockDim.x)
+    rows[offsets[b] + j] = (int64_t)row[j / page_size] * page_size + j % page_size;
+}
+
+}  // namespace
+
+hipError_t launch_split_merge(const MergeArgs& a, hipStream_t stream) {
+  if (a.n_reduce == 0) return hipSuccess;
+  const int R = a.Sq * a.N;
+  const dim3 grid(a.n_reduce, (R + 3) / 4), block(256);
+  hipLaunchKernelGGL(split_merge_kernel, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_two(void* out, float* out_lse, const void* prefix_o, const float* prefix_lse,
+                            const void* suffix_o, const float* suffix_lse, int64_t rows, int32_t D,
+                            bool fp32, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  hipLaunchKernelGGL(merge_two_kernel, grid, block, 0, stream, out, out_lse, prefix_o, prefix_lse,
+                     suffix_o, suffix_lse, rows, D, (int)fp32);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const int32_t* block_table, int64_t bt_s, const int32_t* seq_lens,
+                              const int64_t* offsets, int32_t B, int32_t page_size, int64_t* rows,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(B), dim3(256), 0, stream, block_table, bt_s, seq_lens,
+                     offsets, page_size, rows);
+  return hipGetLastError();
+}
+
+}  // namespace mla

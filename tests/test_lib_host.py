@@ -1,0 +1,131 @@
+"""CPU-side checks of the C-ABI library: exported symbols, the host planner against the
+oracle's re-derivation (bit-exact), and argument validation that fails before any HIP call."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from tests._lib import ROOT, ensure_built
+
+ensure_built()
+from mla_paged_decode_03_amd import api  # noqa: E402
+from oracle import plan as PL  # noqa: E402
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "mla_decode.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _header_functions()
+    assert {"mla_decode_plan", "mla_decode_run", "mla_absorb_q", "mla_up_v",
+            "merge_attn_states", "mla_plan_destroy", "mla_last_error"} <= set(names)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", api.LIB_PATH], text=True)
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(api.exported_symbols()) == set(names)
+
+
+def _oracle_work(seq_lens, Sq, N, C):
+    p = PL.split_plan(seq_lens, Sq, N, C)
+    work = np.array(p["items"], dtype=np.int32).reshape(-1, 5)
+    red = np.array(p["reduce"], dtype=np.int32).reshape(-1, 3)
+    return work, red, p["num_parts"], p["num_partials"]
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_host_plan_bit_exact_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 400))
+    L = rng.integers(0, 33000, size=B)
+    special = np.array([0, 1, 63, 64, 65, 127, 128, 4096, 32768])
+    k = int(rng.integers(0, B + 1))
+    L[:k] = rng.choice(special, size=k)
+    rng.shuffle(L)
+    Sq = int(rng.integers(1, 9))
+    N = int(rng.integers(1, 129))
+    Cu = int(rng.choice([1, 3, 8, 80, 256, 304]))
+    w, r, npart, npartial = api.mla_plan_compute_host(L, Sq, N, Cu)
+    ow, orr, onp, onpl = _oracle_work(L, Sq, N, Cu)
+    assert np.array_equal(w, ow)
+    assert np.array_equal(r, orr)
+    assert (npart, npartial) == (onp, onpl)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv3", "longtail", "verify", "fp8"])
+def test_host_plan_bit_exact_workloads(name):
+    from mla_paged_decode_03_amd import inputs as gen
+    w = gen.workload(name)
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    L = gen.draw_seq_lens(w, rng)
+    got = api.mla_plan_compute_host(L, w.Sq, w.N, 256)
+    exp = _oracle_work(L, w.Sq, w.N, 256)
+    for a, b in zip(got, exp):
+        assert np.array_equal(np.asarray(a), np.asarray(b))
+
+
+def _plan_rc(**kw):
+    args = dict(seq_lens=np.array([10], np.int32), B=1, Sq=1, N=16, Lkv=512, R=64, ps=16, mp=4,
+                dt=api.MLA_DT_BF16, cus=1)
+    args.update(kw)
+    sl = np.ascontiguousarray(args["seq_lens"], dtype=np.int32)
+    h = C.c_void_p()
+    ws = C.c_size_t()
+    rc = api._lib.mla_decode_plan(sl.ctypes.data_as(api._pi32), args["B"], args["Sq"], args["N"],
+                                  args["Lkv"], args["R"], args["ps"], args["mp"], args["dt"],
+                                  args["cus"], None, C.byref(h), C.byref(ws))
+    return rc, api.mla_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Lkv=256), api.MLA_ERR_UNSUPPORTED),
+    (dict(R=32), api.MLA_ERR_UNSUPPORTED),
+    (dict(N=129), api.MLA_ERR_UNSUPPORTED),
+    (dict(N=0), api.MLA_ERR_UNSUPPORTED),
+    (dict(Sq=9), api.MLA_ERR_UNSUPPORTED),
+    (dict(Sq=0), api.MLA_ERR_UNSUPPORTED),
+    (dict(dt=7), api.MLA_ERR_UNSUPPORTED),
+    (dict(B=0), api.MLA_ERR_INVALID_ARG),
+    (dict(ps=0), api.MLA_ERR_INVALID_ARG),
+    (dict(seq_lens=np.array([65], np.int32)), api.MLA_ERR_INVALID_ARG),  # > 4 pages of 16
+    (dict(seq_lens=np.array([-1], np.int32)), api.MLA_ERR_INVALID_ARG),
+])
+def test_plan_argument_errors(kw, code):
+    rc, msg = _plan_rc(**kw)
+    assert rc == code and msg
+
+
+def test_null_and_destroy_paths():
+    assert api._lib.mla_plan_destroy(None) == api.MLA_OK
+    h = C.c_void_p()
+    ws = C.c_size_t()
+    assert api._lib.mla_decode_plan(None, 1, 1, 16, 512, 64, 16, 4, 0, 1, None, C.byref(h),
+                                    C.byref(ws)) == api.MLA_ERR_INVALID_ARG
+    rc = api._lib.mla_decode_run(None, None, 0, 0, None, 0, 0, None, None, 0, 0, 0, None, 0, None,
+                                 1.0, 1.0, None, 0, 0, None, None, 0, None)
+    assert rc == api.MLA_ERR_INVALID_ARG and "plan" in api.mla_last_error()
+    assert api._lib.mla_absorb_q(None, None, None, 1, 1, 128, 512, None) == api.MLA_ERR_INVALID_ARG
+    assert api._lib.mla_up_v(None, None, None, 1, 1, 512, 128, None) == api.MLA_ERR_INVALID_ARG
+    assert api._lib.merge_attn_states(None, None, None, None, None, None, 1, 1, 8, 0, None) == \
+        api.MLA_ERR_INVALID_ARG
+    assert api._lib.mla_plan_export(None, None, None, None, None) == api.MLA_ERR_INVALID_ARG
+    assert api._lib.mla_debug_gather_rows(None, None, 0, None, None) == api.MLA_ERR_INVALID_ARG
+
+
+def test_gemm_and_merge_shape_errors():
+    buf = (C.c_uint8 * 4096)()
+    p = C.cast(buf, C.c_void_p).value
+    p16 = (p + 15) // 16 * 16
+    assert api._lib.mla_absorb_q(p16, p16, p16, 1, 1, 12, 512, None) == api.MLA_ERR_UNSUPPORTED
+    assert api._lib.mla_up_v(p16, p16, p16, 1, 1, 512, 12, None) == api.MLA_ERR_UNSUPPORTED
+    assert api._lib.merge_attn_states(p16, None, p16, p16, p16, p16, 1, 1, 12, 0, None) == \
+        api.MLA_ERR_UNSUPPORTED
+    assert api._lib.merge_attn_states(p16, None, p16, p16, p16, p16, 1, 1, 16, 5, None) == \
+        api.MLA_ERR_UNSUPPORTED
+    assert api._lib.mla_absorb_q(p16 + 2, p16, p16, 1, 1, 128, 512, None) == api.MLA_ERR_INVALID_ARG
