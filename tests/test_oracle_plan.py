@@ -67,8 +67,10 @@ def test_plan_workload_shapes():
     p = _check([256], 1, 16, 256)
     assert p["items"] == [(0, 0, 0, 256, -1)] and p["reduce"] == []
     p = _check([4096] * 32, 4, 128, 256)
-    assert PL.head_groups(4, 128) == 4 and p["num_parts"] <= 64
-    assert all(n == 2 for (_, _, n) in p["reduce"])
+    assert PL.head_groups(4, 128) == 8 and p["num_parts"] <= 32
+    assert p["reduce"] == [] and p["num_parts"] == 32  # one request (65 granules of cost) per part
+    p = _check([4096] * 8, 1, 128, 256)
+    assert PL.head_groups(1, 128) == 2 and all(n == 16 for (_, _, n) in p["reduce"])
     p = _check([0, 0, 5], 1, 128, 256)
     assert [it[1:] for it in p["items"]] == [(0, 0, 0, -1), (1, 0, 0, -1), (2, 0, 5, -1)]
 
@@ -76,7 +78,7 @@ def test_plan_workload_shapes():
 def test_plan_is_independent_of_head_count_when_groups_match():
     L = np.random.default_rng(9).integers(1, 9000, size=50)
     a = PL.split_plan(L, 1, 16, 256)
-    b = PL.split_plan(L, 1, 128, 256)
+    b = PL.split_plan(L, 1, 64, 256)
     assert a["items"] == b["items"] and a["reduce"] == b["reduce"]
 
 
