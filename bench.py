@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of MLA paged decode (absorbed latent-MQA) on one MI355X.
+
+One step is one MLA decode layer call on one batch: [absorb] -> decode attend ->
+split reduce -> [up-projection] (the bracketed stages only for workloads that
+carry q_nope / W_UK / W_UV).  The split plan is built once per batch before the
+timed region, as a serving stack builds it once per batch for all layers; its
+host time is reported as plan_host_us.  Inputs are resident in HBM.
+
+Prints one JSON line: tokens/s of the whole step, plus the roofline of the
+dominant kernel (the decode kernel, timed with HIP events on the stream it is
+launched on) and the CPU fp64 oracle timed on a bounded sample of the same batch.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3|longtail|verify|fp8|tiny]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+# BLAS threads of the CPU-baseline leg: every core this process may use (set before numpy loads).
+if "OMP_NUM_THREADS" not in os.environ:
+    os.environ["OMP_NUM_THREADS"] = str(len(os.sched_getaffinity(0)))
+os.environ.setdefault("OPENBLAS_NUM_THREADS", os.environ["OMP_NUM_THREADS"])
+
+import numpy as np  # noqa: E402
+
+METRIC = "MLA decode tokens/s, HBM GB/s and MFMA TFLOP/s (% roofline), DSV3 shape"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+LKV, ROPE = 512, 64
+WANT_LSE = {"tiny": True, "dsv3": False, "longtail": False, "verify": False, "fp8": True}
+
+
+def algorithmic_work(w, seq_lens, with_lse):
+    """Bytes the decode must move and flops it must do (no split-partial traffic)."""
+    L = seq_lens.astype(np.int64)
+    ekv = 1 if w.kv_dtype == "fp8" else 2
+    T, N, Sq = w.T, w.N, w.Sq
+    kv = int(L.sum()) * (LKV + ROPE) * ekv
+    q = T * N * (LKV + ROPE) * 2
+    o = T * N * LKV * 2
+    lse = T * N * 4 if with_lse else 0
+    meta = int(((L + w.page_size - 1) // w.page_size).sum()) * 4 + 4 * w.B
+    visible = sum(max(0, int(l) - (Sq - 1) + t) for l in L for t in range(Sq))
+    flops = 2 * (LKV + ROPE + LKV) * N * visible
+    out = dict(kv_bytes=kv, bytes=kv + q + o + lse + meta, flops=flops, visible_keys=visible)
+    if w.absorb:
+        # each of absorb / up-projection: 2*T*N*P*Lkv flops; weights + activations once
+        out["gemm_flops"] = 2 * (2 * T * N * w.P * LKV)
+        out["gemm_bytes"] = 2 * (T * N * w.P + LKV * N * w.P + T * N * LKV) * 2
+    return out
+
+
+def cpu_baseline(inp, o_gpu, budget_s):
+    """The fp64 oracle, as it stands, on the first requests of the batch until budget_s."""
+    from oracle import attention as A
+    from oracle.formats import bf16_to_f64
+    w = inp.w
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        cores = int(os.environ["OMP_NUM_THREADS"])
+    if w.absorb:
+        q_nope = bf16_to_f64(inp.q_nope)
+        W_UK = bf16_to_f64(inp.W_UK)
+        W_UV = bf16_to_f64(inp.W_UV)
+    else:
+        ql = bf16_to_f64(inp.q)
+    qpe = bf16_to_f64(inp.q_pe)
+    done, t_used = [], 0.0
+    errs = []
+    for b in range(w.B):
+        sl = slice(b * w.Sq, (b + 1) * w.Sq)
+        t0 = time.perf_counter()
+        if w.absorb:
+            ql_b = A.absorb(q_nope[sl], W_UK)
+        else:
+            ql_b = ql[sl]
+        o, _ = A.latent_attention(ql_b, qpe[sl], inp.cache, w.kv_dtype, inp.kv_scale,
+                                  inp.block_table[b:b + 1], inp.seq_lens[b:b + 1], w.Sq, w.scale)
+        if w.absorb:
+            o = A.up_proj(o, W_UV)
+        t_used += time.perf_counter() - t0
+        done.append(b)
+        d = o_gpu[sl] - o
+        errs.append((float(np.max(np.abs(d))), float(np.sum(d * d)), float(np.sum(o * o))))
+        if t_used >= budget_s:
+            break
+    toks = len(done) * w.Sq
+    max_abs = max(e[0] for e in errs)
+    rel_l2 = float(np.sqrt(sum(e[1] for e in errs) / max(sum(e[2] for e in errs), 1e-300)))
+    base = dict(value=toks / t_used, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"first {len(done)} of {w.B} requests ({toks} query tokens, "
+                       f"{int(inp.seq_lens[done].sum())} keys), {t_used:.1f} s of fp64 numpy")
+    return base, dict(requests=len(done), max_abs=max_abs, rel_l2=rel_l2)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (no collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_paged_decode_03_amd import api
+    from mla_paged_decode_03_amd import inputs as gen
+
+    w = gen.workload(args.workload)
+    t_gen = time.perf_counter()
+    inp = gen.generate(w)
+    t_gen = time.perf_counter() - t_gen
+    dev = "cuda"
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    with_lse = WANT_LSE.get(w.name, False)
+    T, N = w.T, w.N
+    q_pe = bf16(inp.q_pe)
+    if w.kv_dtype == "bf16":
+        cache = bf16(inp.cache)
+        dt = api.MLA_DT_BF16
+    else:
+        cache = torch.from_numpy(inp.cache).view(torch.float8_e4m3fn).to(dev)
+        dt = api.MLA_DT_FP8_E4M3FN
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seq_lens).to(dev)
+    o_lat = torch.empty((T, N, LKV), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, N), dtype=torch.float32, device=dev) if with_lse else None
+    if w.absorb:
+        q_nope = bf16(inp.q_nope)
+        W_UK = bf16(inp.W_UK)
+        W_UV = bf16(inp.W_UV)
+        ql = torch.empty((T, N, LKV), dtype=torch.bfloat16, device=dev)
+        o_up = torch.empty((T, N, w.V), dtype=torch.bfloat16, device=dev)
+    else:
+        ql = bf16(inp.q)
+
+    t0 = time.perf_counter()
+    plan = api.mla_decode_plan(inp.seq_lens, w.Sq, N, w.page_size, inp.block_table.shape[1], dt)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    work, red = api.mla_plan_export(plan)
+
+    def step(ev=None):
+        if w.absorb:
+            api.mla_absorb_q(q_nope, W_UK, ql)
+        if ev is not None:
+            ev[0].record()
+        api.mla_decode_attend(plan, ql, q_pe, cache, bt, sl, w.scale, inp.kv_scale, o_lat, lse, ws)
+        if ev is not None:
+            ev[1].record()
+        api.mla_decode_reduce(plan, o_lat, lse, ws)
+        if ev is not None:
+            ev[2].record()
+        if w.absorb:
+            api.mla_up_v(o_lat, W_UV, o_up)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    ms_per_step = t_total / K * 1e3
+    dec_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    red_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+
+    # Cold-cache timing of the decode kernel: a 1 GiB write evicts L2 and the 256 MB MALL.
+    cold_us = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(float(i))
+            step(cev[i])
+        torch.cuda.synchronize()
+        cold_us = float(np.mean([e[0].elapsed_time(e[1]) for e in cev])) * 1e3
+        del flush
+
+    work_alg = algorithmic_work(w, inp.seq_lens, with_lse)
+    hbm_gbs = work_alg["bytes"] / (dec_us * 1e-6) / 1e9
+    tflops = work_alg["flops"] / (dec_us * 1e-6) / 1e12
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if work_alg["flops"] / work_alg["bytes"] < ridge else "mfma"
+    if bound == "hbm":
+        roof = dict(bound="hbm", achieved=round(hbm_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(hbm_gbs / HBM_PEAK_GBS, 4), traffic=None)
+    else:
+        roof = dict(bound="mfma", achieved=round(tflops, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tflops / BF16_PEAK_TFLOPS, 4), traffic=None)
+    t_roof_us = max(work_alg["bytes"] / (HBM_PEAK_GBS * 1e9), work_alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-kv/bf16-mfma", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "N": N, "Lkv": LKV, "R": ROPE,
+                   "page_size": w.page_size, "kv_dtype": w.kv_dtype,
+                   "seq_lens": f"{w.seqlen_kind}[{w.seqlen_lo},{w.seqlen_hi}] seed {w.seed}",
+                   "sum_keys": int(inp.seq_lens.sum()), "absorb_up": bool(w.absorb),
+                   "lse": with_lse},
+        "roofline": roof,
+        "decode_kernel_us": round(dec_us, 2), "reduce_kernel_us": round(red_us, 2),
+        "decode_kernel_cold_us": None if cold_us is None else round(cold_us, 2),
+        "hbm_gbps": round(hbm_gbs, 1), "tflops": round(tflops, 1),
+        "frac_hbm": round(hbm_gbs / HBM_PEAK_GBS, 4), "frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "frac_roofline": round(t_roof_us / dec_us, 4),
+        "algorithmic": work_alg, "plan_host_us": round(plan_us, 1),
+        "plan": {"parts": int(work[:, 0].max()) + 1 if len(work) else 0, "segments": int(len(work)),
+                 "split_requests": int(len(red)), "workspace_bytes": int(plan.workspace_bytes)},
+        "input_gen_s": round(t_gen, 2),
+    }
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        o_dev = o_up if w.absorb else o_lat
+        o_np = o_dev.float().cpu().numpy().astype(np.float64)
+        base, parity = cpu_baseline(inp, o_np, args.cpu_budget)
+        line["cpu_baseline"] = base
+        line["parity_sample"] = parity
+    plan.destroy()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -66,7 +66,7 @@ typedef struct mla_plan_s* mla_plan;
  * parts of near-equal cost; a request cut between parts is computed as
  * partial states merged by LSE (the combiner of the mla/common.py docstring,
  * "Chunked Prefill").  Rows of a request are Sq*N (row r = t*N + h); they are
- * processed in head groups of up to 128 consecutive rows.
+ * processed in head groups of up to 64 consecutive rows.
  *
  *  seq_lens_host      [B] host int32, keys per request (>= 0), including the
  *                     Sq new tokens; query row t of a request sees keys
@@ -117,8 +117,9 @@ int mla_plan_destroy(mla_plan plan);
  *  o_latent  [B*Sq, N, 512] bf16 output, strides o_s_tok, o_s_head.
  *  lse       [B*Sq, N] fp32 output (contiguous) or NULL.
  *  workspace device scratch of at least the plan's workspace_bytes (may be NULL if 0).
- * Errors: INVALID_ARG (nulls, bad strides, misaligned pointers: bf16 tensors need
- * 16-byte aligned rows, fp8 8-byte), WORKSPACE, HIP.
+ * Errors: INVALID_ARG (nulls, bad strides, misaligned pointers: query and output
+ * rows must be 16-byte aligned, cache rows 16-byte (bf16) or 8-byte (fp8)),
+ * WORKSPACE, HIP.
  */
 int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
                    const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head,
@@ -127,6 +128,27 @@ int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int6
                    int64_t block_table_s_req, const int32_t* seq_lens, float scale,
                    float kv_scale, void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_attend / mla_decode_reduce -- the two phases of mla_decode_run,
+ * for callers that schedule or time them separately (the persistent decode of
+ * rocm_aiter_mla likewise runs attention over work items and then a reduce
+ * over split requests).  attend takes exactly the arguments of mla_decode_run
+ * and writes the final output of unsplit requests plus the partial states of
+ * split ones into the workspace; reduce merges those partial states into
+ * o_latent / lse.  reduce is a no-op when the plan splits nothing.  Running
+ * attend then reduce on one stream is identical to mla_decode_run.
+ */
+int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok,
+                      int64_t q_nope_s_head, const void* q_pe, int64_t q_pe_s_tok,
+                      int64_t q_pe_s_head, const void* cache_kv_c, const void* cache_k_pe,
+                      int64_t cache_s_page, int64_t cache_s_tok, int32_t num_pages,
+                      const int32_t* block_table, int64_t block_table_s_req,
+                      const int32_t* seq_lens, float scale, float kv_scale, void* o_latent,
+                      int64_t o_s_tok, int64_t o_s_head, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+int mla_decode_reduce(mla_plan plan, void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mla_absorb_q -- ql_nope[t,h,l] = sum_p q_nope[t,h,p] * W_UK[l,h,p].

@@ -40,6 +40,9 @@ _SIGS = {
     "mla_plan_destroy": [_vp],
     "mla_decode_run": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i32, _vp, _i64,
                        _vp, _f32, _f32, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mla_decode_attend": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i32, _vp,
+                          _i64, _vp, _f32, _f32, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mla_decode_reduce": [_vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
     "mla_absorb_q": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp],
     "mla_up_v": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp],
     "merge_attn_states": [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp],
@@ -135,12 +138,8 @@ def _need(t, dtypes, name):
         raise TypeError(f"{name} must be a device tensor")
 
 
-def mla_decode_run(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale: float,
-                   kv_scale: float, o_latent, lse=None, workspace=None, stream=None,
-                   cache_k_pe=None):
-    """q_nope [T,N,512] bf16, q_pe [T,N,64] bf16, cache [pages, page_size, 576] (bf16 or fp8;
-    or the kv_c part when cache_k_pe is given), block_table [B, max_pages] int32,
-    seq_lens [B] int32 (device), o_latent [T,N,512] bf16, lse [T,N] fp32 or None."""
+def _decode_args(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale, kv_scale,
+                 o_latent, lse, workspace, stream, cache_k_pe):
     bf, f8 = torch.bfloat16, (torch.float8_e4m3fn, torch.uint8)
     _need(q_nope, (bf,), "q_nope")
     _need(q_pe, (bf,), "q_pe")
@@ -156,15 +155,41 @@ def mla_decode_run(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale
         raise ValueError("the last dimension of every tensor must be contiguous")
     esz = cache.element_size()
     kpe_ptr = cache.data_ptr() + LKV * esz if cache_k_pe is None else cache_k_pe.data_ptr()
-    ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.mla_decode_run(
-        plan.handle, q_nope.data_ptr(), q_nope.stride(0), q_nope.stride(1),
-        q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1),
-        cache.data_ptr(), kpe_ptr, cache.stride(0), cache.stride(1), cache.shape[0],
-        block_table.data_ptr(), block_table.stride(0), seq_lens.data_ptr(),
-        float(scale), float(kv_scale), o_latent.data_ptr(), o_latent.stride(0), o_latent.stride(1),
-        _ptr(lse), ws_ptr, ws_bytes, _stream(stream)))
+    return (plan.handle, q_nope.data_ptr(), q_nope.stride(0), q_nope.stride(1),
+            q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1),
+            cache.data_ptr(), kpe_ptr, cache.stride(0), cache.stride(1), cache.shape[0],
+            block_table.data_ptr(), block_table.stride(0), seq_lens.data_ptr(),
+            float(scale), float(kv_scale), o_latent.data_ptr(), o_latent.stride(0),
+            o_latent.stride(1), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def mla_decode_run(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale: float,
+                   kv_scale: float, o_latent, lse=None, workspace=None, stream=None,
+                   cache_k_pe=None):
+    """q_nope [T,N,512] bf16, q_pe [T,N,64] bf16, cache [pages, page_size, 576] (bf16 or fp8;
+    or the kv_c part when cache_k_pe is given), block_table [B, max_pages] int32,
+    seq_lens [B] int32 (device), o_latent [T,N,512] bf16, lse [T,N] fp32 or None."""
+    _check(_lib.mla_decode_run(*_decode_args(plan, q_nope, q_pe, cache, block_table, seq_lens, scale,
+                                             kv_scale, o_latent, lse, workspace, stream, cache_k_pe)))
+
+
+def mla_decode_attend(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale: float,
+                      kv_scale: float, o_latent, lse=None, workspace=None, stream=None,
+                      cache_k_pe=None):
+    """First phase of mla_decode_run (the decode kernel); same arguments."""
+    _check(_lib.mla_decode_attend(*_decode_args(plan, q_nope, q_pe, cache, block_table, seq_lens,
+                                                scale, kv_scale, o_latent, lse, workspace, stream,
+                                                cache_k_pe)))
+
+
+def mla_decode_reduce(plan: Plan, o_latent, lse=None, workspace=None, stream=None):
+    """Second phase of mla_decode_run: merges the partial states of split requests."""
+    _need(o_latent, (torch.bfloat16,), "o_latent")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.mla_decode_reduce(plan.handle, o_latent.data_ptr(), o_latent.stride(0),
+                                  o_latent.stride(1), _ptr(lse), _ptr(workspace), ws_bytes,
+                                  _stream(stream)))
 
 
 def _need_contig_bf16(*ts):

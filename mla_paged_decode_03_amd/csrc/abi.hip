@@ -46,6 +46,8 @@ extern "C" {
 
 const char* mla_last_error(void) { return g_err.c_str(); }
 
+static int check_workspace(mla_plan plan, void* workspace, size_t workspace_bytes);
+
 static int validate_dims(int32_t B, int32_t Sq, int32_t N, int32_t Lkv, int32_t R, int32_t page_size,
                          int32_t max_pages, int32_t kv_dtype) {
   if (B < 1) return fail(MLA_ERR_INVALID_ARG, "B must be >= 1");
@@ -200,7 +202,7 @@ int mla_plan_export(mla_plan plan, int32_t* work_host, int32_t* n_items, int32_t
   return MLA_OK;
 }
 
-int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
+int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
                    const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head,
                    const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
                    int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
@@ -225,13 +227,11 @@ int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int6
     return fail(MLA_ERR_INVALID_ARG, "queries need 16-byte aligned rows (pointer and strides)");
   if (!aligned(cache_kv_c, cal) || !aligned(cache_k_pe, cal) || cache_s_page % 8 || cache_s_tok % 8)
     return fail(MLA_ERR_INVALID_ARG, "cache rows must be aligned to 8 elements");
-  if (!aligned(o_latent, 8) || o_s_tok % 4 || o_s_head % 4)
-    return fail(MLA_ERR_INVALID_ARG, "o_latent needs 8-byte aligned rows");
-  if (plan->ws_bytes > 0) {
-    if (!workspace || workspace_bytes < plan->ws_bytes)
-      return fail(MLA_ERR_WORKSPACE, "workspace smaller than the plan requires (" +
-                                         std::to_string(plan->ws_bytes) + " bytes)");
-    if (!aligned(workspace, 16)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (!aligned(o_latent, 16) || o_s_tok % 8 || o_s_head % 8)
+    return fail(MLA_ERR_INVALID_ARG, "o_latent needs 16-byte aligned rows (pointer and strides)");
+  {
+    const int wrc = check_workspace(plan, workspace, workspace_bytes);
+    if (wrc) return wrc;
   }
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -271,20 +271,60 @@ int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int6
   hipStream_t s = (hipStream_t)stream;
   e = mla::launch_decode(a, fp8, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return MLA_OK;
+}
+
+static int check_workspace(mla_plan plan, void* workspace, size_t workspace_bytes) {
+  if (plan->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+      return fail(MLA_ERR_WORKSPACE, "workspace smaller than the plan requires (" +
+                                         std::to_string(plan->ws_bytes) + " bytes)");
+    if (!aligned(workspace, 16)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  return MLA_OK;
+}
+
+int mla_decode_reduce(mla_plan plan, void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARG, "null plan");
+  if (!o_latent) return fail(MLA_ERR_INVALID_ARG, "null o_latent");
+  if (o_s_tok < 1 || o_s_head < 1) return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  if (!aligned(o_latent, 16) || o_s_tok % 8 || o_s_head % 8)
+    return fail(MLA_ERR_INVALID_ARG, "o_latent needs 16-byte aligned rows for the merge");
+  const int rc = check_workspace(plan, workspace, workspace_bytes);
+  if (rc) return rc;
+  const auto& hp = plan->host;
+  const size_t R = (size_t)hp.Sq * hp.N;
   mla::MergeArgs m{};
   m.reduce = plan->d_buf + plan->off_reduce;
   m.n_reduce = (int32_t)hp.reduce.size() / 3;
-  m.ws_o = a.ws_o;
-  m.ws_lse = a.ws_lse;
-  m.o = a.o;
+  m.ws_o = (float*)workspace;
+  m.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * R * mla::kLkv * 4) : nullptr;
+  m.o = (uint16_t*)o_latent;
   m.o_s_tok = o_s_tok;
   m.o_s_head = o_s_head;
   m.lse = lse;
   m.Sq = hp.Sq;
   m.N = hp.N;
-  e = mla::launch_split_merge(m, s);
+  hipError_t e = mla::launch_split_merge(m, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return MLA_OK;
+}
+
+int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
+                   const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head,
+                   const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
+                   int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
+                   int64_t block_table_s_req, const int32_t* seq_lens, float scale,
+                   float kv_scale, void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = mla_decode_attend(plan, q_nope, q_nope_s_tok, q_nope_s_head, q_pe, q_pe_s_tok, q_pe_s_head,
+                             cache_kv_c, cache_k_pe, cache_s_page, cache_s_tok, num_pages, block_table,
+                             block_table_s_req, seq_lens, scale, kv_scale, o_latent, o_s_tok, o_s_head,
+                             lse, workspace, workspace_bytes, stream);
+  if (rc) return rc;
+  if (plan->host.reduce.empty()) return MLA_OK;
+  return mla_decode_reduce(plan, o_latent, o_s_tok, o_s_head, lse, workspace, workspace_bytes, stream);
 }
 
 int mla_absorb_q(const void* q_nope, const void* W_UK, void* ql_nope, int32_t T, int32_t N,

@@ -3,175 +3,250 @@
 // Computes, for every query row of every request, softmax attention over the
 // request's cache rows [kv_c | k_pe] with value kv_c (vLLM mla/common.py
 // module docstring, "Data-Movement Friendly Approach").  One workgroup of four
-// waves owns one head group (up to 128 query rows of one request) of one plan
-// part and walks the part's segments (request, key range) in 32-key tiles:
+// waves owns one head group (up to 64 query rows of one request) of one plan
+// part and walks the part's segments (request, key range) in 32-key tiles.
+// The head groups of a part run on one XCD, so a tile read from HBM by one of
+// them is served to the others from that XCD's L2.
 //
-//  stage    every thread loads 16-byte pieces of 8 keys (and one rope piece)
-//           from HBM, writes them row-major into the K tile in LDS and, after
-//           an 8x8 transpose in registers, key-packed into the V^T tile (the
-//           first 512 columns of the same rows are the values).  The loads for
-//           the next tile are issued before this tile is consumed.
+//  load     a tile is 32 cache rows of 576 bf16 (36 KB) in LDS: a latent part
+//           [32 rows][512] (1 KB per row) and a rope part [32 rows][64], both
+//           row-major with a 16-byte-chunk XOR swizzle.  bf16 caches go HBM ->
+//           LDS with global_load_lds_dwordx4 (no VGPRs), one instruction per
+//           latent row, so the row address is wave-uniform; up to 3 tiles are
+//           in flight ahead of the one being computed.  fp8 caches go through
+//           VGPRs, are widened to bf16 and written to LDS.  Keys past the
+//           segment end load a valid key instead and get probability 0, so
+//           unused page slots and block_table entries are never read.
 //  QK^T     wave w < ceil(rows/32) computes S^T[32 keys x 32 rows] for rows
-//           32w..32w+31 with v_mfma_f32_32x32x16_bf16: A = K tile (LDS),
+//           32w..32w+31 with v_mfma_f32_32x32x16_bf16: A = K rows from LDS,
 //           B = the wave's query rows, held in VGPRs for the whole segment.
-//  softmax  online, fp32, log2 domain; row max / sum over the two lane halves
-//           of the MFMA layout.  P (bf16) goes to LDS.  Each row's reference
-//           max is fixed by its first tile with a visible key and O is never
-//           rescaled: if a later tile exceeds the reference by more than
-//           2^64, the workgroup restarts the segment with the raised maxima
-//           (a bounded number of times), so P <= 2^64 and O stays in AGPRs
-//           as a plain MFMA accumulator.
+//  softmax  fp32, log2 domain; row max / sum over the two lane halves of the
+//           MFMA layout.  Each row's reference max is fixed by its first tile
+//           with a visible key and O is never rescaled: if a later tile exceeds
+//           the reference by more than 2^64 the workgroup restarts the segment
+//           with the raised maxima (a bounded number of times), so P <= 2^64
+//           and O stays in AGPRs as a plain MFMA accumulator.  P (bf16) -> LDS.
 //  P.V      wave w owns output columns 128w..128w+127 of every row and
-//           accumulates O^T += V^T . P^T (A = V^T tile, B = P), fp32 in VGPRs.
+//           accumulates O^T += V^T . P^T.  V^T fragments come straight from the
+//           row-major K tile through ds_read_b64_tr_b16 (4 keys x 16 columns
+//           per 16-lane group), P fragments from LDS.
 //  epilogue o = O * kv_scale / l, lse = ln(sum exp) to the output, or fp32
 //           partial states to the workspace when the request is split.
-//
-// Keys at or past the segment end are never loaded (zeros go to LDS) and get
-// probability 0, so unused page slots and block_table entries are never read.
 #include "common.h"
 #include "kernels.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace mla {
 
 namespace {
 
 constexpr int kTile = 32;
-constexpr int kKRowBytes = kHead * 2;                 // 1152: one bf16 key row
-constexpr int kKStageBytes = kTile * kKRowBytes;      // 36864
-constexpr int kVtStageBytes = 4 * kLkv * 16;          // 32768: [4 key chunks][512 cols][8 keys]
-constexpr int kKOff = 0;
-constexpr int kVtOff = 2 * kKStageBytes;              // 73728
-constexpr int kPOff = kVtOff + 2 * kVtStageBytes;     // 139264: [128 rows][4 chunks][8 keys] bf16
-constexpr int kEllOff = kPOff + 128 * 64;             // 147456: row sums for the epilogue
-constexpr int kFlagOff = kEllOff + 128 * 4;           // 147968: per-wave restart request
-constexpr int kSmemBytes = kFlagOff + 16;             // 147984
-// A logit may exceed its row's reference max by at most this (log2 units)
-// before the segment is restarted with a higher reference.
-constexpr float kMaxOvershoot = 64.f;
+constexpr int kLatRow = kLkv * 2;                 // 1024: latent part of a bf16 key row
+constexpr int kRopeRow = kRope * 2;               // 128: rope part
+constexpr int kRopeOff = kTile * kLatRow;         // 32768: rope part of a stage
+constexpr int kStageBytes = kRopeOff + kTile * kRopeRow;  // 36864
+constexpr int kMaxStages = 4;
+constexpr int kPOff = kMaxStages * kStageBytes;   // 147456: P [128 rows][4 chunks][8 keys] bf16
+constexpr int kEllOff = kPOff + 128 * 64;         // 155648: row sums for the epilogue
+constexpr int kFlagOff = kEllOff + 128 * 4;       // 156160: per-wave restart request
+constexpr int kSmemBytes = kFlagOff + 16;         // 156176
+constexpr float kMaxOvershoot = 64.f;             // log2 units
 
-// Key (0..31 within the tile) held at element e of 8-key chunk q of the V^T and
-// P layouts.  The order matches where a lane of the 32x32 S^T accumulator
-// finds its keys, so P needs no shuffle between the two MFMAs.
-__device__ __forceinline__ int chunk_key(int q, int e) {
-  return 16 * (q >> 1) + 4 * (q & 1) + (e & 3) + 8 * (e >> 2);
+__shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// The lane index, produced by a volatile instruction pair so that per-lane values
+// derived from it are recomputed where they are used instead of being hoisted out
+// of the loops and kept live (VGPRs are the scarce resource of this kernel).
+__device__ __forceinline__ int lane_id() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
 }
 
-// Byte offsets inside the LDS tiles (XOR swizzles keep the 16-byte lane
-// accesses of both the staging writes and the MFMA operand reads spread over
-// all banks).
-__device__ __forceinline__ int k_off(int key, int chunk) {
-  return key * kKRowBytes + ((chunk ^ (key & 7)) << 4);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
 }
-__device__ __forceinline__ int vt_off(int q, int col) {
-  return q * (kLkv * 16) + (((col & ~7) | ((col & 7) ^ ((col >> 3) & 7))) << 4);
+
+// HBM -> LDS, 16 bytes per lane: lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
 }
-__device__ __forceinline__ int p_off(int row, int q) {
+// Waits until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// A tile is PER DMA instructions per wave; wait until at most `newer` tiles are pending.
+template <int PER>
+__device__ __forceinline__ void wait_tiles(int newer) {
+  switch (newer) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<PER>(); break;
+    default: wait_vm<2 * PER>(); break;
+  }
+}
+// Same, with a uniform 64-bit global base and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16_s(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_base)
+               : "memory", "m0");
+}
+// Workgroup barrier that also orders this wave's LDS writes (and does not drain vmcnt).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Byte offset in a stage of logical 16-byte chunk c (0..71) of key row `key`: chunk
+// c ^ (key & 7) of the latent row (c < 64) or of the rope row (c >= 64).
+__device__ __forceinline__ int tile_off(int key, int c) {
+  return c < 64 ? key * kLatRow + ((c ^ (key & 7)) << 4)
+                : kRopeOff + key * kRopeRow + (((c - 64) ^ (key & 7)) << 4);
+}
+
+__device__ __forceinline__ int p_off(int row, int q) {  // P tile [row][chunk q of 8 keys]
   return row * 64 + ((q ^ ((row >> 1) & 3)) << 4);
 }
 
-template <bool FP8>
-struct Stage;
-
-template <>
-struct Stage<false> {
-  u32x4_t v[8];  // 8 keys x 8 latent columns
-  u32x4_t r;     // one rope piece
+struct Seg {
+  int b, ks, ke, pidx;
 };
-template <>
-struct Stage<true> {
-  u32x2_t v[8];
-  u32x2_t r;
-};
+__device__ __forceinline__ Seg load_seg(const int32_t* segs, int si) {
+  return Seg{ld_uniform(segs + 4 * si), ld_uniform(segs + 4 * si + 1), ld_uniform(segs + 4 * si + 2),
+             ld_uniform(segs + 4 * si + 3)};
+}
 
-// Element offsets (within the cache) of the rows of this thread's keys in a
-// tile: 8 latent keys of chunk q and the rope key rk.  When page_size is a
-// multiple of 32 the whole tile lies in one page and a single (uniform)
-// block_table lookup serves it; otherwise every key looks up its own page,
-// all lookups issued before any data load.
+// Tile cursor over the part's segments: (segment index, first key of the tile).
+struct Cursor {
+  int si, ts;
+};
+__device__ __forceinline__ Cursor first_tile(const int32_t* segs, int si, int s_end) {
+  for (; si < s_end; ++si) {
+    const Seg s = load_seg(segs, si);
+    if (s.ke > s.ks) return Cursor{si, s.ks};
+  }
+  return Cursor{s_end, 0};
+}
+__device__ __forceinline__ Cursor next_tile(const int32_t* segs, Cursor c, int s_end) {
+  const Seg s = load_seg(segs, c.si);
+  if (c.ts + kTile < s.ke) return Cursor{c.si, c.ts + kTile};
+  return first_tile(segs, c.si + 1, s_end);
+}
+
+// Byte offset (from the cache base) of key row j of a request; esz = element size.
+// UNIFORM: j is the same in every lane (scalar block_table load).
+template <bool UNIFORM>
+__device__ __forceinline__ int64_t row_bytes(const DecodeArgs& a, const int32_t* bt_row, int j, int esz) {
+  const unsigned ps = (unsigned)a.page_size;
+  const int page = UNIFORM ? ld_uniform(bt_row + (unsigned)j / ps) : bt_row[(unsigned)j / ps];
+  return ((int64_t)page * a.s_page + (int64_t)((unsigned)j % ps) * a.s_tok) * esz;
+}
+
+// bf16: issue this wave's DMA loads of tile (b, keys ts..ts+31 clipped at ke) into
+// `stage`: wave w loads key rows 8w..8w+7, one instruction per latent row (lane =
+// physical chunk) and the rope parts of its 8 rows (lane = 8 rows x 8 chunks).  A key
+// past ke loads key ke-1 instead.  Returns nothing; PER_TILE instructions per wave.
 template <bool PAGED32>
-__device__ __forceinline__ void tile_rows(const DecodeArgs& a, const int32_t* bt_row, int ts, int ke,
-                                          int q, int rk, int64_t (&off)[9]) {
-  const int ps = a.page_size;
-  if constexpr (PAGED32) {
-    const int page = ld_uniform(bt_row + (unsigned)ts / (unsigned)ps);
-    const int64_t base = (int64_t)page * a.s_page + (int64_t)((unsigned)ts % (unsigned)ps) * a.s_tok;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) off[e] = base + (int64_t)chunk_key(q, e) * a.s_tok;
-    off[8] = base + (int64_t)rk * a.s_tok;
-  } else {
-    int pg[9];
-    unsigned jj[9];
-#pragma unroll
-    for (int e = 0; e < 9; ++e) {
-      const int j = ts + (e < 8 ? chunk_key(q, e) : rk);
-      jj[e] = (unsigned)min(j, ke - 1);  // clamp: keys past ke are not loaded
-      pg[e] = bt_row[jj[e] / (unsigned)ps];
-    }
-#pragma unroll
-    for (int e = 0; e < 9; ++e) off[e] = (int64_t)pg[e] * a.s_page + (int64_t)(jj[e] % (unsigned)ps) * a.s_tok;
-  }
-}
-
-// Issues the global loads of one tile: keys [ts, ts+32) of request b, clipped at ke.
-template <bool FP8, bool PAGED32>
-__device__ __forceinline__ void load_tile(const DecodeArgs& a, Stage<FP8>& st, int b, int ts, int ke,
-                                          int tid) {
+__device__ __forceinline__ void issue_tile_bf16(const DecodeArgs& a, int b, int ts, int ke, uint32_t stage,
+                                                int w, int lane) {
   const int32_t* bt_row = a.block_table + (int64_t)b * a.bt_s;
-  const int q = tid >> 6, cg = tid & 63;
-  const int rk = tid >> 3, rc = tid & 7;
-  int64_t off[9];
-  tile_rows<PAGED32>(a, bt_row, ts, ke, q, rk, off);
-  if constexpr (!FP8) {
-    const uint16_t* kvc = (const uint16_t*)a.kv_c + 8 * cg;
-    const uint16_t* kpe = (const uint16_t*)a.k_pe + 8 * rc;
+  const char* kvc = (const char*)a.kv_c;
+  const char* kpe = (const char*)a.k_pe;
+  const int kmax = ke - ts - 1;
+  const int64_t s_tok2 = a.s_tok * 2;
+  int64_t tile_base = 0;
+  if constexpr (PAGED32) tile_base = row_bytes<true>(a, bt_row, ts, 2);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      st.v[e] = (ts + chunk_key(q, e) < ke) ? *(const u32x4_t*)(kvc + off[e]) : u32x4_t{0, 0, 0, 0};
-    st.r = (ts + rk < ke) ? *(const u32x4_t*)(kpe + off[8]) : u32x4_t{0, 0, 0, 0};
+  for (int i = 0; i < 8; ++i) {
+    const int key = 8 * w + i;  // wave-uniform
+    const int kc = min(key, kmax);
+    const int64_t roff = PAGED32 ? tile_base + kc * s_tok2 : row_bytes<true>(a, bt_row, ts + kc, 2);
+    dma16_s(kvc + roff, (uint32_t)((lane ^ (key & 7)) << 4),
+            __builtin_amdgcn_readfirstlane(stage + key * kLatRow));
+  }
+  // rope: lane = (row 8w + lane/8, physical chunk lane%8)
+  const int rk = 8 * w + (lane >> 3);
+  const uint32_t rlds = __builtin_amdgcn_readfirstlane(stage + kRopeOff + 8 * w * kRopeRow);
+  if constexpr (PAGED32) {
+    const int kc = min(rk, kmax);
+    const uint32_t voff = (uint32_t)(kc * s_tok2) + ((((lane & 7) ^ (rk & 7))) << 4);
+    dma16_s(kpe + tile_base, voff, rlds);
   } else {
-    const uint8_t* kvc = (const uint8_t*)a.kv_c + 8 * cg;
-    const uint8_t* kpe = (const uint8_t*)a.k_pe + 8 * rc;
+    // rows may sit on different pages: one instruction per row with only its 8 lanes active
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      st.v[e] = (ts + chunk_key(q, e) < ke) ? *(const u32x2_t*)(kvc + off[e]) : u32x2_t{0, 0};
-    st.r = (ts + rk < ke) ? *(const u32x2_t*)(kpe + off[8]) : u32x2_t{0, 0};
-  }
-}
-
-__device__ __forceinline__ u32x4_t widen8(u32x2_t w) {
-  const u32x2_t lo = fp8x4_to_bf16x4(w[0]);
-  const u32x2_t hi = fp8x4_to_bf16x4(w[1]);
-  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-}
-
-// Writes the staged tile into LDS: K rows (all 576 columns) and V^T.
-template <bool FP8>
-__device__ __forceinline__ void store_tile(char* smem, int stage, const Stage<FP8>& st, int tid) {
-  char* kt = smem + kKOff + stage * kKStageBytes;
-  char* vt = smem + kVtOff + stage * kVtStageBytes;
-  const int q = tid >> 6, cg = tid & 63;
-  u32x4_t r[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if constexpr (FP8) r[e] = widen8(st.v[e]); else r[e] = st.v[e];
-    *(u32x4_t*)(kt + k_off(chunk_key(q, e), cg)) = r[e];
-  }
-  {
-    const int rk = tid >> 3, rc = tid & 7;
-    u32x4_t rr;
-    if constexpr (FP8) rr = widen8(st.r); else rr = st.r;
-    *(u32x4_t*)(kt + k_off(rk, 64 + rc)) = rr;
-  }
-  // 8x8 transpose: out[c] holds column 8*cg+c of the 8 keys of chunk q.
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    u32x4_t o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t x = r[2 * k][c >> 1], y = r[2 * k + 1][c >> 1];
-      o[k] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+    for (int i = 0; i < 8; ++i) {
+      const int key = 8 * w + i;
+      const int kc = min(key, kmax);
+      const int64_t roff = row_bytes<true>(a, bt_row, ts + kc, 2);
+      if ((lane >> 3) == i) dma16_s(kpe + roff, (uint32_t)((((lane & 7) ^ (key & 7))) << 4), rlds);
     }
-    *(u32x4_t*)(vt + vt_off(q, 8 * cg + c)) = o;
+  }
+}
+
+// fp8: per thread 9 chunks of 8 bytes (8 dims); chunk u = tid + 256 i of the tile.
+template <bool PAGED32>
+__device__ __forceinline__ void load_tile_fp8(const DecodeArgs& a, int b, int ts, int ke, int tid,
+                                              u32x2_t (&v)[9]) {
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.bt_s;
+  const char* kvc = (const char*)a.kv_c;
+  const int64_t pe_delta = (const char*)a.k_pe - kvc;
+  const int kmax = ke - ts - 1;
+  int64_t tile_base = 0;
+  if constexpr (PAGED32) tile_base = row_bytes<true>(a, bt_row, ts, 1);
+  int64_t off[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int u = tid + 256 * i;
+    const int kk = min(u / 72, kmax), c = u - 72 * (u / 72);
+    const int64_t o = PAGED32 ? tile_base + (int64_t)kk * a.s_tok : row_bytes<false>(a, bt_row, ts + kk, 1);
+    off[i] = o + ((c < 64) ? (int64_t)(8 * c) : pe_delta + 8 * (c - 64));
+  }
+#pragma unroll
+  for (int i = 0; i < 9; ++i) v[i] = *(const u32x2_t*)(kvc + off[i]);
+}
+
+__device__ __forceinline__ void store_tile_fp8(char* stage, int tid, const u32x2_t (&v)[9]) {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int u = tid + 256 * i;
+    const int kk = u / 72, c = u - 72 * (u / 72);
+    const u32x2_t lo = fp8x4_to_bf16x4(v[i][0]);
+    const u32x2_t hi = fp8x4_to_bf16x4(v[i][1]);
+    *(u32x4_t*)(stage + tile_off(kk, c)) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  }
+}
+
+// 8 bf16 of V^T (column of this lane, 8 keys) from the row-major tile: two transposing reads.
+__device__ __forceinline__ u32x4_t read_vt(const char* p) {
+  const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)p);
+  const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)(p + 8 * kLatRow));
+  u32x4_t r;
+  r[0] = (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+  r[1] = (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+  r[2] = (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+  r[3] = (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+  return r;
+}
+
+// Issues up to `count` tiles at the cursor: DMA into the next stages (bf16) or the
+// staging registers (fp8).
+template <bool FP8, bool PAGED32, int NST>
+__device__ __forceinline__ void issue_ahead(const DecodeArgs& a, const int32_t* segs, int s_end,
+                                            Cursor& pf, int& issued, int count, int tid, int w, int l,
+                                            u32x2_t (&fstage)[9]) {
+  for (int k = 0; k < count; ++k) {
+    if (pf.si >= s_end) break;
+    const Seg s = load_seg(segs, pf.si);
+    if constexpr (FP8)
+      load_tile_fp8<PAGED32>(a, s.b, pf.ts, s.ke, 64 * w + lane_id(), fstage);
+    else
+      issue_tile_bf16<PAGED32>(a, s.b, pf.ts, s.ke, lds_addr(smem) + (issued % NST) * kStageBytes, w,
+                               lane_id());
+    pf = next_tile(segs, pf, s_end);
+    issued++;
   }
 }
 
@@ -179,8 +254,9 @@ __device__ __forceinline__ void store_tile(char* smem, int stage, const Stage<FP
 
 template <bool FP8, bool PAGED32, int NRB>
 __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l32 = l & 31, hh = l >> 5;
+  constexpr int NST = FP8 ? 2 : kMaxStages;
+  const int tid = threadIdx.x, l = tid & 63, l32 = l & 31, hh = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
 
   // Workgroups are dealt round-robin to the 8 XCDs; keep the head groups of
   // one part on one XCD so that they share its L2 for the part's keys.
@@ -192,13 +268,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
   const int R = a.Sq * a.N;
   const int row0 = hg * kGroupRows;
   const int RG = min(kGroupRows, R - row0);  // rows of this group; NRB = ceil(RG / 32) or more
-
+  const int32_t* segs = a.segs;
   const int s_beg = ld_uniform(a.part_begin + part), s_end = ld_uniform(a.part_begin + part + 1);
-  const int32_t* segs = a.segs;  // [num_segs][4]: req, kv_start, kv_end, partial
-
-  Stage<FP8> st;
-  int stage = 0;
-  bool have = false;  // st holds the next tile to store
 
   float* ell_l = (float*)(smem + kEllOff);
   int* flag_l = (int*)(smem + kFlagOff);
@@ -206,9 +277,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
   const int qrow_loc = 32 * w + l32;  // this lane's query row in QK^T (waves w < NRB)
   const bool qk_wave = w < NRB;
 
+  // ---- load pipeline (wave-uniform state) ----
+  Cursor pf = first_tile(segs, s_beg, s_end);  // next tile to load
+  int issued = 0, consumed = 0;
+  u32x2_t fstage[9];  // fp8 staging registers
+
+  issue_ahead<FP8, PAGED32, NST>(a, segs, s_end, pf, issued, NST - 1, tid, w, l, fstage);
+
   for (int si = s_beg; si < s_end; ++si) {
-    const int b = ld_uniform(segs + 4 * si), ks = ld_uniform(segs + 4 * si + 1);
-    const int ke = ld_uniform(segs + 4 * si + 2), pidx = ld_uniform(segs + 4 * si + 3);
+    const Seg sg = load_seg(segs, si);
+    const int b = sg.b, ks = sg.ks, ke = sg.ke, pidx = sg.pidx;
     const int L = ld_uniform(a.seq_lens + b);
 
     // Query rows of this wave: B operand of S^T = K . Q^T, 36 x 8 bf16 per lane.
@@ -232,8 +310,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
       }
     }
 
-    float m_ref = -INFINITY;  // reference max of this row (log2 units)
-    float m_seen = -INFINITY; // largest logit seen so far
+    float m_ref = -INFINITY;   // reference max of this row (log2 units)
+    float m_seen = -INFINITY;  // largest logit seen so far
     float l_run = 0.f;
     f32x16_t O[4][NRB];
     for (;;) {  // one pass over the segment; repeated only after a restart request
@@ -247,41 +325,49 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
       bool restart = false;
 
       for (int ts = ks; ts < ke; ts += kTile) {
-        if (!have) load_tile<FP8, PAGED32>(a, st, b, ts, ke, tid);
-        store_tile<FP8>(smem, stage, st, tid);
-        // Prefetch the next tile: later in this segment or the first tile of the
-        // next segment that has keys.
-        have = false;
-        if (ts + kTile < ke) {
-          load_tile<FP8, PAGED32>(a, st, b, ts + kTile, ke, tid);
-          have = true;
+        char* stage = smem + (consumed % NST) * kStageBytes;
+        if constexpr (FP8) {
+          // the stage was last read two tiles ago, before the previous barriers
+          store_tile_fp8(stage, 64 * w + lane_id(), fstage);
+          issue_ahead<FP8, PAGED32, NST>(a, segs, s_end, pf, issued, 1, tid, w, l, fstage);
+          barrier_lds();
         } else {
-          for (int sn = si + 1; sn < s_end; ++sn) {
-            const int nb = ld_uniform(segs + 4 * sn), nks = ld_uniform(segs + 4 * sn + 1);
-            const int nke = ld_uniform(segs + 4 * sn + 2);
-            if (nke > nks) {
-              load_tile<FP8, PAGED32>(a, st, nb, nks, nke, tid);
-              have = true;
-              break;
-            }
-          }
+          wait_tiles<PAGED32 ? 9 : 16>(issued - consumed - 1);  // this tile's DMA has landed
+          barrier_lds();                      // ... for every wave; the previous stage is free
+          issue_ahead<FP8, PAGED32, NST>(a, segs, s_end, pf, issued, 1, tid, w, l, fstage);
         }
-        __syncthreads();
 
         if (qk_wave) {
-          const char* kt = smem + kKOff + stage * kKStageBytes;
+          // QK A operand: key r32, logical chunk 2k + h2 at byte kq_off[k & 3] + 128 (k >> 2)
+          // (latent, k < 32) or kr_off[k & 3] (rope, k >= 32).
+          const int ln = lane_id(), r32 = ln & 31, h2 = ln >> 5;
+          int kq_off[4], kr_off[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            kq_off[m] = r32 * kLatRow + (((2 * m + h2) ^ (r32 & 7)) << 4);
+            kr_off[m] = kRopeOff + r32 * kRopeRow + (((2 * m + h2) ^ (r32 & 7)) << 4);
+          }
+          // 36 MFMAs over the 576 dims; K fragments stream through a 4-deep ring so that
+          // LDS latency overlaps the MFMA chain.
+          auto kaddr = [&](int k) -> const u32x4_t* {
+            return (const u32x4_t*)(stage + (k < 32 ? kq_off[k & 3] + 128 * (k >> 2) : kr_off[k & 3]));
+          };
+          u32x4_t kb[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) kb[k] = *kaddr(k);
           f32x16_t sacc;
 #pragma unroll
           for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
           for (int k = 0; k < 36; ++k) {
-            const u32x4_t kf = *(const u32x4_t*)(kt + k_off(l32, 2 * k + hh));
+            const u32x4_t kf = kb[k & 3];
+            if (k + 4 < 36) kb[k & 3] = *kaddr(k + 4);
             sacc = mfma32(kf, qr[k], sacc);
           }
           float mx = -INFINITY;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int j = ts + 8 * (v >> 2) + 4 * hh + (v & 3);
+            const int j = ts + 8 * (v >> 2) + 4 * h2 + (v & 3);
             sacc[v] = (j < lim) ? sacc[v] * a.qk_scale_log2 : -INFINITY;
             mx = fmaxf(mx, sacc[v]);
           }
@@ -301,46 +387,59 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
           }
           psum += __shfl_xor(psum, 32);
           l_run += psum;
-          // keys 8s'..8s'+7 of this lane's accumulator form P chunk q = 2s' + hh
-          *(u32x4_t*)(smem + kPOff + p_off(qrow_loc, hh)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-          *(u32x4_t*)(smem + kPOff + p_off(qrow_loc, 2 + hh)) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
+          // keys 8s'..8s'+7 of this lane's accumulator form P chunk q = 2s' + h2
+          *(u32x4_t*)(smem + kPOff + p_off(32 * w + r32, h2)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+          *(u32x4_t*)(smem + kPOff + p_off(32 * w + r32, 2 + h2)) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
           const bool any = __any(over);
           if (l == 0) flag_l[w] = any ? 1 : 0;
         }
-        __syncthreads();
+        barrier_lds();
 
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) restart |= (flag_l[rb] != 0);
         if (restart) break;  // uniform over the workgroup
 
-        // O^T[cols of wave w][rows] += V^T . P^T
+        // O^T[cols of wave w][rows] += V^T . P^T, 16 keys (one MFMA k-step) at a time.
+        // V^T through ds_read_b64_tr_b16: 16-lane group g = lane/16 covers columns
+        // c0 = 128w + 32cb + 16(g&1) and keys t0..t0+3, t0 = 16s + 4h (+8 for elements
+        // 4..7); lane j = lane%16 addresses key t0 + j/4, columns c0 + 4(j&3) .. +3 and
+        // receives keys t0..t0+3 of column c0 + j.
+        const int pl = lane_id(), p32 = pl & 31, ph = pl >> 5;
+        int vt_off[2];
         {
-          const char* vt = smem + kVtOff + stage * kVtStageBytes;
-          u32x4_t pf[NRB][2];
+          const int g = pl >> 4, j = pl & 15;
+          const int key = 4 * ph + (j >> 2);
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-              pf[rb][s] = *(const u32x4_t*)(smem + kPOff + p_off(32 * rb + l32, 2 * s + hh));
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            const int col = 128 * w + 32 * cb + l32;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const u32x4_t vf = *(const u32x4_t*)(vt + vt_off(2 * s + hh, col));
-#pragma unroll
-              for (int rb = 0; rb < NRB; ++rb) O[cb][rb] = mfma32(vf, pf[rb][s], O[cb][rb]);
-            }
+          for (int cbp = 0; cbp < 2; ++cbp) {
+            const int col = 128 * w + 32 * cbp + 16 * (g & 1) + 4 * (j & 3);
+            vt_off[cbp] = key * kLatRow + (((col >> 3) ^ (key & 7)) << 4) + 8 * ((col >> 2) & 1);
           }
         }
-        stage ^= 1;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          u32x4_t pfr[NRB], vfr[4];
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            pfr[rb] = *(const u32x4_t*)(smem + kPOff + p_off(32 * rb + p32, 2 * s + ph));
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            vfr[cb] = read_vt(stage + vt_off[cb & 1] + 128 * (cb >> 1) + 16 * s * kLatRow);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) O[cb][rb] = mfma32(vfr[cb], pfr[rb], O[cb][rb]);
+        }
+        consumed++;
       }
       if (!restart) break;
-      // Raise every row's reference to the largest logit seen and start over.
+      // Raise every row's reference to the largest logit seen and start the segment
+      // over: drain the loads in flight and refill the pipeline from its first tile.
       m_ref = m_seen;
-      stage ^= 1;
-      have = false;
-      __syncthreads();  // nobody still reads the flags or this stage
+      wait_vm<0>();
+      barrier_lds();
+      consumed = issued;
+      pf = first_tile(segs, si, s_end);
+      issue_ahead<FP8, PAGED32, NST>(a, segs, s_end, pf, issued, NST - 1, tid, w, l, fstage);
     }
 
     // Epilogue.  QK waves publish the row sums and write the LSE.
@@ -359,10 +458,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
         }
       }
     }
-    __syncthreads();
+    barrier_lds();
+    const int el = lane_id(), e32 = el & 31, eh = el >> 5;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      const int rl = 32 * rb + l32;
+      const int rl = 32 * rb + e32;
       if (rl >= RG) continue;
       const int r = row0 + rl;
       const float lsum = ell_l[rl];
@@ -374,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = 128 * w + 32 * cb + 8 * g + 4 * hh;
+            const int col = 128 * w + 32 * cb + 8 * g + 4 * eh;
             const f32x16_t& acc = O[cb][rb];
             u32x2_t pk;
             pk[0] = pack_bf16x2(acc[4 * g] * f, acc[4 * g + 1] * f);
@@ -387,7 +487,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = 128 * w + 32 * cb + 8 * g + 4 * hh;
+            const int col = 128 * w + 32 * cb + 8 * g + 4 * eh;
             const f32x16_t& acc = O[cb][rb];
             *(f32x4_t*)(prow + col) =
                 f32x4_t{acc[4 * g] * f, acc[4 * g + 1] * f, acc[4 * g + 2] * f, acc[4 * g + 3] * f};
@@ -395,21 +495,20 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
       }
     }
   }
+  wait_vm<0>();  // no DMA outlives the workgroup
 }
 
 template <bool FP8, bool PAGED32>
 static hipError_t launch_nrb(const DecodeArgs& a, int nrb, dim3 grid, hipStream_t stream) {
   switch (nrb) {
     case 1: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 1>), grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 2>), grid, dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 3>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 4>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 2>), grid, dim3(256), 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
-  // Every head group but the last has 128 rows; the last may be smaller, but a
+  // Every head group but the last has 64 rows; the last may be smaller, but a
   // group never needs more row blocks than the first one, so one instance serves all.
   const int R = a.Sq * a.N;
   const int nrb = (min(R, kGroupRows) + 31) / 32;
