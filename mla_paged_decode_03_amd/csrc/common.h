@@ -52,6 +52,27 @@ __device__ __forceinline__ T ld_uniform(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
+// Combines a value with the one held by lane l ^ 32 (the other half of the MFMA
+// layout).  v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; with both operands holding x, each lane ends up with its
+// own value in one result and its partner's in the other.  The second operand passes
+// through an empty asm so that the compiler cannot see the two operands are equal
+// (it folds the second result into the first when it can).
+__device__ __forceinline__ uint2 half_pair(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("" : "+v"(b));
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return make_uint2(r[0], r[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+  const uint2 r = half_pair(x);
+  return fmaxf(__builtin_bit_cast(float, r.x), __builtin_bit_cast(float, r.y));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const uint2 r = half_pair(x);
+  return __builtin_bit_cast(float, r.x) + __builtin_bit_cast(float, r.y);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

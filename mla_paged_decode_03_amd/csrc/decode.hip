@@ -58,6 +58,12 @@ __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
+// Keeps an MFMA accumulator in AGPRs.  The constraint also makes the compiler select
+// the AGPR form of every MFMA in the kernel, so accumulators that only MFMAs update
+// stay in the accumulation registers instead of being copied to VGPRs and back.
+template <typename T>
+__device__ __forceinline__ void pin_agpr(T& x) { asm("" : "+a"(x)); }
+
 // The lane index, produced by a volatile instruction pair so that per-lane values
 // derived from it are recomputed where they are used instead of being hoisted out
 // of the loops and kept live (VGPRs are the scarce resource of this kernel).
@@ -98,11 +104,22 @@ __device__ __forceinline__ void dma16_s(const void* gbase, uint32_t voff, uint32
 // Workgroup barrier that also orders this wave's LDS writes (and does not drain vmcnt).
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Byte offset in a stage of logical 16-byte chunk c (0..71) of key row `key`: chunk
-// c ^ (key & 7) of the latent row (c < 64) or of the rope row (c >= 64).
+// LDS swizzles (64 banks of 4 bytes: a 16-byte chunk's bank group is its index mod 16).
+// Latent rows are 1 KB apart, so every row starts in the same bank group; logical chunk
+// c of key k sits in physical chunk c ^ lat_swz(k).  lat_swz is a bijection on k & 15,
+// so the 16 keys of one ds_read_b128 cycle (same c) hit 16 distinct bank groups, and for
+// any 4 consecutive keys 4a..4a+3 it gives 4 distinct chunk pairs, so the transposing
+// V reads (4 keys x 2 chunks per 16-lane group) are conflict-free too.
+__device__ __forceinline__ int lat_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
+// Rope rows are 128 B (8 chunks): keys 2m and 2m+1 share bank groups 0..7 / 8..15, so
+// the keys of one parity need distinct chunks.
+__device__ __forceinline__ int rope_swz(int k) { return (k >> 1) & 7; }
+
+// Byte offset in a stage of logical 16-byte chunk c (0..71) of key row `key`: the
+// latent row (c < 64) or the rope row (c >= 64), swizzled as above.
 __device__ __forceinline__ int tile_off(int key, int c) {
-  return c < 64 ? key * kLatRow + ((c ^ (key & 7)) << 4)
-                : kRopeOff + key * kRopeRow + (((c - 64) ^ (key & 7)) << 4);
+  return c < 64 ? key * kLatRow + ((c ^ lat_swz(key)) << 4)
+                : kRopeOff + key * kRopeRow + (((c - 64) ^ rope_swz(key)) << 4);
 }
 
 __device__ __forceinline__ int p_off(int row, int q) {  // P tile [row][chunk q of 8 keys]
@@ -162,7 +179,7 @@ __device__ __forceinline__ void issue_tile_bf16(const DecodeArgs& a, int b, int 
     const int key = 8 * w + i;  // wave-uniform
     const int kc = min(key, kmax);
     const int64_t roff = PAGED32 ? tile_base + kc * s_tok2 : row_bytes<true>(a, bt_row, ts + kc, 2);
-    dma16_s(kvc + roff, (uint32_t)((lane ^ (key & 7)) << 4),
+    dma16_s(kvc + roff, (uint32_t)((lane ^ lat_swz(key)) << 4),
             __builtin_amdgcn_readfirstlane(stage + key * kLatRow));
   }
   // rope: lane = (row 8w + lane/8, physical chunk lane%8)
@@ -170,7 +187,7 @@ __device__ __forceinline__ void issue_tile_bf16(const DecodeArgs& a, int b, int 
   const uint32_t rlds = __builtin_amdgcn_readfirstlane(stage + kRopeOff + 8 * w * kRopeRow);
   if constexpr (PAGED32) {
     const int kc = min(rk, kmax);
-    const uint32_t voff = (uint32_t)(kc * s_tok2) + ((((lane & 7) ^ (rk & 7))) << 4);
+    const uint32_t voff = (uint32_t)(kc * s_tok2) + ((((lane & 7) ^ rope_swz(rk))) << 4);
     dma16_s(kpe + tile_base, voff, rlds);
   } else {
     // rows may sit on different pages: one instruction per row with only its 8 lanes active
@@ -179,7 +196,7 @@ __device__ __forceinline__ void issue_tile_bf16(const DecodeArgs& a, int b, int 
       const int key = 8 * w + i;
       const int kc = min(key, kmax);
       const int64_t roff = row_bytes<true>(a, bt_row, ts + kc, 2);
-      if ((lane >> 3) == i) dma16_s(kpe + roff, (uint32_t)((((lane & 7) ^ (key & 7))) << 4), rlds);
+      if ((lane >> 3) == i) dma16_s(kpe + roff, (uint32_t)((((lane & 7) ^ rope_swz(key))) << 4), rlds);
     }
   }
 }
@@ -217,12 +234,13 @@ __device__ __forceinline__ void store_tile_fp8(char* stage, int tid, const u32x2
   }
 }
 
-// 8 bf16 of V^T (column of this lane, 8 keys) from the row-major tile: two transposing reads.
-__device__ __forceinline__ u32x4_t read_vt(const char* p) {
+// 8 bf16 of V^T (column of this lane, 8 keys) from the row-major tile: two transposing
+// reads, p0 for keys t0..t0+3 and p1 for keys t0+8..t0+11.
+__device__ __forceinline__ u32x4_t read_vt(const char* p0, const char* p1) {
   const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)p);
+      (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)p0);
   const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)(p + 8 * kLatRow));
+      (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)p1);
   u32x4_t r;
   r[0] = (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
   r[1] = (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
@@ -303,10 +321,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
         for (int k = 0; k < 32; ++k) qr[k] = *(const u32x4_t*)(qn + 16 * k);
 #pragma unroll
         for (int k = 0; k < 4; ++k) qr[32 + k] = *(const u32x4_t*)(qp + 16 * k);
+        // A wait the compiler sees: the query loads are complete before the tile loop,
+        // so it places no vmcnt waits there (they would also count the DMA loads in
+        // flight and drain the prefetch pipeline).  s_waitcnt vmcnt(0).
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         lim = min(ke, L - (a.Sq - 1) + t);
       } else {
+        // padding rows: zero queries give zero logits; their probabilities only reach
+        // output rows that are never stored
 #pragma unroll
         for (int k = 0; k < 36; ++k) qr[k] = u32x4_t{0, 0, 0, 0};
+        lim = ke;
       }
     }
 
@@ -318,9 +343,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NRB; ++j)
+        for (int j = 0; j < NRB; ++j) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) O[i][j][v] = 0.f;
+          pin_agpr(O[i][j]);
+        }
       l_run = 0.f;
       bool restart = false;
 
@@ -338,19 +365,20 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
         }
 
         if (qk_wave) {
-          // QK A operand: key r32, logical chunk 2k + h2 at byte kq_off[k & 3] + 128 (k >> 2)
-          // (latent, k < 32) or kr_off[k & 3] (rope, k >= 32).
+          // QK A operand: key r32, logical chunk 2k + h2 at byte kq_off[k & 7] + 256 (k >> 3)
+          // (latent, k < 32; the swizzle only permutes chunks within a 16-chunk group) or
+          // kr_off[k & 3] (rope, k >= 32).
           const int ln = lane_id(), r32 = ln & 31, h2 = ln >> 5;
-          int kq_off[4], kr_off[4];
+          int kq_off[8], kr_off[4];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            kq_off[m] = r32 * kLatRow + (((2 * m + h2) ^ (r32 & 7)) << 4);
-            kr_off[m] = kRopeOff + r32 * kRopeRow + (((2 * m + h2) ^ (r32 & 7)) << 4);
-          }
+          for (int m = 0; m < 8; ++m) kq_off[m] = r32 * kLatRow + (((2 * m + h2) ^ lat_swz(r32)) << 4);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            kr_off[m] = kRopeOff + r32 * kRopeRow + (((2 * m + h2) ^ rope_swz(r32)) << 4);
           // 36 MFMAs over the 576 dims; K fragments stream through a 4-deep ring so that
           // LDS latency overlaps the MFMA chain.
           auto kaddr = [&](int k) -> const u32x4_t* {
-            return (const u32x4_t*)(stage + (k < 32 ? kq_off[k & 3] + 128 * (k >> 2) : kr_off[k & 3]));
+            return (const u32x4_t*)(stage + (k < 32 ? kq_off[k & 7] + 256 * (k >> 3) : kr_off[k & 3]));
           };
           u32x4_t kb[4];
 #pragma unroll
@@ -364,28 +392,35 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
             if (k + 4 < 36) kb[k & 3] = *kaddr(k + 4);
             sacc = mfma32(kf, qr[k], sacc);
           }
+          // Logits in log2 units are c * s (c = scale * log2 e > 0); masked keys get -inf.
+          // Tiles entirely inside every row's window skip the masking.
+          const float c = a.qk_scale_log2;
+          if (!__all(ts + kTile <= lim)) {
+            const int rem = lim - ts - 4 * h2;  // key 8(v/4) + 4 h2 + v%4 is visible iff < lim - ts
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (8 * (v >> 2) + (v & 3) >= rem) sacc[v] = -INFINITY;
+          }
           float mx = -INFINITY;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int j = ts + 8 * (v >> 2) + 4 * h2 + (v & 3);
-            sacc[v] = (j < lim) ? sacc[v] * a.qk_scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sacc[v]);
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
+          mx = half_max(mx) * c;
           m_seen = fmaxf(m_seen, mx);
           if (m_ref == -INFINITY) m_ref = mx;  // first visible keys: O and l are still 0
           const bool over = mx > m_ref + kMaxOvershoot;
           const bool dead = (m_ref == -INFINITY);
           float psum = 0.f;
           uint32_t pk[8];
+          const float nm = dead ? 0.f : -m_ref;
 #pragma unroll
           for (int v = 0; v < 16; v += 2) {
-            const float p0 = dead ? 0.f : fast_exp2(sacc[v] - m_ref);
-            const float p1 = dead ? 0.f : fast_exp2(sacc[v + 1] - m_ref);
+            // exp2(-inf) = 0 covers masked keys and rows without visible keys (c * s = -inf)
+            const float p0 = fast_exp2(fmaf(sacc[v], c, nm));
+            const float p1 = fast_exp2(fmaf(sacc[v + 1], c, nm));
             psum += p0 + p1;
             pk[v >> 1] = pack_bf16x2(p0, p1);
           }
-          psum += __shfl_xor(psum, 32);
+          psum = half_sum(psum);
           l_run += psum;
           // keys 8s'..8s'+7 of this lane's accumulator form P chunk q = 2s' + h2
           *(u32x4_t*)(smem + kPOff + p_off(32 * w + r32, h2)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
@@ -405,14 +440,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
         // 4..7); lane j = lane%16 addresses key t0 + j/4, columns c0 + 4(j&3) .. +3 and
         // receives keys t0..t0+3 of column c0 + j.
         const int pl = lane_id(), p32 = pl & 31, ph = pl >> 5;
-        int vt_off[2];
+        int vt_off[2][4];  // [key half (+0 / +8)][column block]
         {
           const int g = pl >> 4, j = pl & 15;
-          const int key = 4 * ph + (j >> 2);
 #pragma unroll
-          for (int cbp = 0; cbp < 2; ++cbp) {
-            const int col = 128 * w + 32 * cbp + 16 * (g & 1) + 4 * (j & 3);
-            vt_off[cbp] = key * kLatRow + (((col >> 3) ^ (key & 7)) << 4) + 8 * ((col >> 2) & 1);
+          for (int kh = 0; kh < 2; ++kh) {
+            const int key = 4 * ph + (j >> 2) + 8 * kh;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              const int col = 128 * w + 32 * cb + 16 * (g & 1) + 4 * (j & 3);
+              vt_off[kh][cb] = key * kLatRow + (((col >> 3) ^ lat_swz(key)) << 4) + 8 * ((col >> 2) & 1);
+            }
           }
         }
 #pragma unroll
@@ -423,11 +461,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
             pfr[rb] = *(const u32x4_t*)(smem + kPOff + p_off(32 * rb + p32, 2 * s + ph));
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb)
-            vfr[cb] = read_vt(stage + vt_off[cb & 1] + 128 * (cb >> 1) + 16 * s * kLatRow);
+            vfr[cb] = read_vt(stage + vt_off[0][cb] + 16 * s * kLatRow, stage + vt_off[1][cb] + 16 * s * kLatRow);
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) O[cb][rb] = mfma32(vfr[cb], pfr[rb], O[cb][rb]);
+            for (int rb = 0; rb < NRB; ++rb) {
+              O[cb][rb] = mfma32(vfr[cb], pfr[rb], O[cb][rb]);
+              pin_agpr(O[cb][rb]);
+            }
         }
         consumed++;
       }
