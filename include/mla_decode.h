@@ -66,7 +66,7 @@ typedef struct mla_plan_s* mla_plan;
  * parts of near-equal cost; a request cut between parts is computed as
  * partial states merged by LSE (the combiner of the mla/common.py docstring,
  * "Chunked Prefill").  Rows of a request are Sq*N (row r = t*N + h); they are
- * processed in head groups of up to 64 consecutive rows.
+ * processed in head groups of up to 128 consecutive rows.
  *
  *  seq_lens_host      [B] host int32, keys per request (>= 0), including the
  *                     Sq new tokens; query row t of a request sees keys

@@ -26,22 +26,24 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)bf16_rne(lo) | ((uint32_t)bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
-// Four OCP e4m3fn bytes -> four bf16 values (two dwords).  Every e4m3fn value
-// is exactly representable in bf16, so the float -> bf16 step is a truncation.
+// Four OCP e4m3fn bytes -> four bf16 values (two dwords), one instruction per pair.
+// Every e4m3fn value is exact in bf16, so a scale of 1 makes the conversion exact.
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
-  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
   u32x2_t r;
-  r[0] = (f32_bits(lo[0]) >> 16) | (f32_bits(lo[1]) & 0xFFFF0000u);
-  r[1] = (f32_bits(hi[0]) >> 16) | (f32_bits(hi[1]) & 0xFFFF0000u);
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   return r;
 }
 

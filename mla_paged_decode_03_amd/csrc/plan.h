@@ -12,7 +12,7 @@ constexpr int kHead = kLkv + kRope;
 constexpr int kGranule = 64;    // keys per planning granule
 constexpr int kSegCost = 1;     // cost of a segment (query load + epilogue), in granules
 constexpr int kMinChunk = 4;    // smallest chunk taken to top up a part that already has work
-constexpr int kGroupRows = 64;  // query rows per head group (one workgroup)
+constexpr int kGroupRows = 128;  // query rows per head group (one workgroup)
 
 struct Segment {
   int32_t req, kv_start, kv_end, partial;  // partial == -1: writes the final output

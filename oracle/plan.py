@@ -10,7 +10,7 @@ within the CU budget), not by the pages.
 
 Rule (integers only):
   g = 64 keys per granule; c0 = 1 granule of cost per segment; MINC = 4.
-  rows per request R = Sq*N; head groups HG = ceil(R / 64).
+  rows per request R = Sq*N; head groups HG = ceil(R / 128).
   part budget P = max(1, floor(C / HG)) for C compute units.
   G_b = ceil(L_b / g); W = sum_b (G_b + c0).
   For target = max(ceil(W / P), c0 + MINC), target + 1, ...: fill parts
@@ -30,7 +30,7 @@ from __future__ import annotations
 GRANULE = 64
 SEG_COST = 1
 MIN_CHUNK = 4
-GROUP_ROWS = 64
+GROUP_ROWS = 128
 
 
 def head_groups(Sq: int, N: int) -> int:

@@ -66,11 +66,14 @@ def test_plan_workload_shapes():
     # a single short request fits one segment; long uniform requests split evenly
     p = _check([256], 1, 16, 256)
     assert p["items"] == [(0, 0, 0, 256, -1)] and p["reduce"] == []
+    # 4 tokens x 128 heads = 4 head groups of 128 rows, so 64 parts for 256 CUs: each
+    # request (64 granules + 1 of segment cost) is cut in two near-equal halves
     p = _check([4096] * 32, 4, 128, 256)
-    assert PL.head_groups(4, 128) == 8 and p["num_parts"] <= 32
-    assert p["reduce"] == [] and p["num_parts"] == 32  # one request (65 granules of cost) per part
+    assert PL.head_groups(4, 128) == 4 and p["num_parts"] == 64
+    assert p["reduce"] == [(b, 2 * b, 2) for b in range(32)]
+    # 128 heads fit one group: 256 parts, the minimum chunk (4 granules) sets the cut
     p = _check([4096] * 8, 1, 128, 256)
-    assert PL.head_groups(1, 128) == 2 and all(n == 16 for (_, _, n) in p["reduce"])
+    assert PL.head_groups(1, 128) == 1 and all(n == 16 for (_, _, n) in p["reduce"])
     p = _check([0, 0, 5], 1, 128, 256)
     assert [it[1:] for it in p["items"]] == [(0, 0, 0, -1), (1, 0, 0, -1), (2, 0, 5, -1)]
 
