@@ -219,14 +219,17 @@ int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, i
   if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
   if (!std::isfinite(scale) || !std::isfinite(kv_scale) || kv_scale <= 0.f)
     return fail(MLA_ERR_INVALID_ARG, "scale and kv_scale must be finite, kv_scale > 0");
-  // 16-byte vector loads of 8 bf16 (8 fp8 bytes for the cache), 8-byte output stores.
+  // 16-byte loads of the queries and of cache pieces (8 bf16 or 16 fp8 values), 8-byte
+  // output stores; the kernel forms the byte offset of a key within a 32-key tile in 32 bits.
   const bool fp8 = plan->kv_dtype == MLA_DT_FP8_E4M3FN;
-  const size_t cal = fp8 ? 8 : 16;
+  const size_t cal = 16;
+  if (cache_s_tok > (int64_t(1) << 24)) return fail(MLA_ERR_INVALID_ARG, "cache_s_tok too large");
   if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || q_nope_s_tok % 8 || q_nope_s_head % 8 ||
       q_pe_s_tok % 8 || q_pe_s_head % 8)
     return fail(MLA_ERR_INVALID_ARG, "queries need 16-byte aligned rows (pointer and strides)");
-  if (!aligned(cache_kv_c, cal) || !aligned(cache_k_pe, cal) || cache_s_page % 8 || cache_s_tok % 8)
-    return fail(MLA_ERR_INVALID_ARG, "cache rows must be aligned to 8 elements");
+  const int64_t cel = fp8 ? 16 : 8;  // elements per 16 bytes
+  if (!aligned(cache_kv_c, cal) || !aligned(cache_k_pe, cal) || cache_s_page % cel || cache_s_tok % cel)
+    return fail(MLA_ERR_INVALID_ARG, "cache rows must be 16-byte aligned (pointers and strides)");
   if (!aligned(o_latent, 16) || o_s_tok % 8 || o_s_head % 8)
     return fail(MLA_ERR_INVALID_ARG, "o_latent needs 16-byte aligned rows (pointer and strides)");
   {

@@ -6,12 +6,15 @@
 // 576-wide latent row, shared by all Sq*N query rows of the request.
 //
 // Work split.  One workgroup (4 waves) per (plan part, head group of up to 128
-// query rows).  Wave w owns rows 32w..32w+31 of the group from end to end:
-// S^T = K.Q^T for its rows, the softmax, and O^T += V^T.P^T over all 512 output
-// columns, with O in the 256 accumulation registers (AGPRs) and P in VGPRs.  The
-// waves share only the key tile in LDS, so there is one barrier per tile.  The head
-// groups of one part are dealt to one XCD, so when Sq*N > 128 a tile that one group
-// reads from HBM reaches the others from that XCD's L2.
+// query rows, NRB = ceil(rows / 32) row blocks).  Per tile of 32 keys:
+//  QK^T     wave w < NRB computes S^T = K.Q^T for rows 32w..32w+31 (its query rows
+//           stay in VGPRs for the whole segment), then the softmax of those rows,
+//           and writes P (bf16) and the rows' rescale factors to LDS.
+//  P.V      after a barrier, wave w accumulates O^T += V^T.P^T for output columns
+//           128w..128w+127 of every row of the group: 4 x NRB accumulator blocks
+//           (up to all 256 AGPRs), reading only its quarter of the value tile.
+// The head groups of one part are dealt to one XCD, so when Sq*N > 128 a tile that
+// one group reads from HBM reaches the others from that XCD's L2.
 //
 // Tiles.  A tile is 32 cache rows.  A bf16 stage in LDS holds the latent part
 // [32][512] (1 KB rows) and the rope part [32][64], each with an XOR swizzle of its
@@ -27,8 +30,9 @@
 //
 // Softmax.  fp32, log2 domain.  Each row keeps a reference maximum m, and p =
 // 2^(c s - m) is accumulated without touching O while the tile maxima stay within
-// 2^8 of m.  A tile that goes further raises m to its maximum and rescales that row
-// of O and its running sum in registers (rare after the first tile of a segment).
+// 2^8 of m.  A tile that goes further raises m to its maximum; the row's running sum
+// is rescaled by the QK wave and its O columns by every wave, with the factor passed
+// through LDS next to P (rare after the first tile of a segment).
 //
 // MFMAs (v_mfma_f32_32x32x16_bf16) are inline asm: only then does the compiler leave
 // all accumulation registers to O.  It does not model MFMA hazards across inline
@@ -54,8 +58,12 @@ constexpr int kRawRopeOff = kTile * kLkv;                 // 16384: rope part of
 constexpr int kRawBytes = kRawRopeOff + kTile * kRope;    // 18432
 constexpr int kRawStages = 4;                             // fp8 cache (plus 2 bf16 stages)
 constexpr int kRawOff = 2 * kStageBytes;                  // 73728
-constexpr int kSmemBytes = kStages * kStageBytes;         // 147456
-static_assert(kRawOff + kRawStages * kRawBytes == kSmemBytes, "fp8 stages fill the bf16 layout");
+constexpr int kStageArea = kStages * kStageBytes;         // 147456
+static_assert(kRawOff + kRawStages * kRawBytes == kStageArea, "fp8 stages fill the bf16 layout");
+constexpr int kPOff = kStageArea;                         // P [128 rows][32 keys] bf16, 64 B rows
+constexpr int kFacOff = kPOff + kGroupRows * 64;          // per-row rescale factor of the tile
+constexpr int kEllOff = kFacOff + kGroupRows * 4;         // per-row sums for the epilogue
+constexpr int kSmemBytes = kEllOff + kGroupRows * 4;      // 156672
 constexpr float kRescaleAt = 8.f;  // log2 units a tile maximum may exceed the reference by
 
 __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
@@ -79,12 +87,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // HBM -> LDS, 16 bytes per lane: lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).
 // 64-bit per-lane address.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 // Same, with a wave-uniform 64-bit base and a 32-bit per-lane byte offset.
 __device__ __forceinline__ void dma16_s(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds_base)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 // Waits until at most N vector-memory operations of this wave are outstanding.
@@ -104,7 +114,12 @@ __device__ __forceinline__ void wait_tiles(int newer) {
   }
 }
 // Workgroup barrier that also orders this wave's LDS accesses (and does not drain vmcnt).
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The lgkmcnt(0) wait is the compiler's own, so it knows that every LDS and scalar load
+// issued before is complete and places no conservative waits after the barrier.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // s_waitcnt lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // ---- MFMA statements (see the header for the wait states) ----
 __device__ __forceinline__ void mfma_first(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
@@ -128,14 +143,16 @@ __device__ __forceinline__ void mfma_acc_a_last(f32x16_t& d, const u32x4_t& a, c
 __device__ __forceinline__ void acc_written(f32x16_t& d) { asm volatile("s_nop 2" : "+a"(d)); }
 // Zeroes the 16 output accumulators in place (0 * 0 + 0 on the MFMA unit), without a
 // zero vector in VGPRs that the compiler would keep live across the loops.
-__device__ __forceinline__ void acc_zero(f32x16_t (&o)[16]) {
+template <int NB>
+__device__ __forceinline__ void acc_zero(f32x16_t (&o)[NB]) {
   u32x4_t z = u32x4_t{0, 0, 0, 0};
   asm volatile("" : "+v"(z));
 #pragma unroll
-  for (int cb = 0; cb < 15; ++cb)
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=&a"(o[cb]) : "v"(z));
+  for (int i = 0; i < NB - 1; ++i)
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=&a"(o[i]) : "v"(z));
   // an empty segment reads the accumulators right away
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0\n\ts_nop 7\n\ts_nop 7" : "=&a"(o[15]) : "v"(z));
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0\n\ts_nop 7\n\ts_nop 7" : "=&a"(o[NB - 1])
+               : "v"(z));
 }
 // Keeps an accumulator in AGPRs up to this point, so that the compiler copies it to
 // VGPRs only where it is read, one block at a time (not all 256 registers at once).
@@ -152,6 +169,10 @@ __device__ __forceinline__ int lat_swz(int k) { return ((k & 3) << 2) | ((k >> 2
 // the keys of one parity need distinct chunks.
 __device__ __forceinline__ int rope_swz(int k) { return (k >> 1) & 7; }
 
+// P row r holds keys in 4 chunks of 16 bytes; chunk q sits at q ^ ((r >> 2) & 3), so the
+// 16 rows of one 16-lane access (same q) cover all 16 bank groups.
+__device__ __forceinline__ int p_off(int r, int q) { return kPOff + r * 64 + ((q ^ ((r >> 2) & 3)) << 4); }
+
 // Byte offset in a bf16 stage of logical 16-byte chunk c (0..71) of key row `key`: the
 // latent row (c < 64) or the rope row (c >= 64), swizzled as above.
 __device__ __forceinline__ int tile_off(int key, int c) {
@@ -167,20 +188,20 @@ __device__ __forceinline__ Seg load_seg(const int32_t* segs, int si) {
              ld_uniform(segs + 4 * si + 3)};
 }
 
-// Tile cursor over the part's segments: (segment index, first key of the tile).
+// Tile cursor over the part's segments: segment index, first key of the tile, and the
+// segment's request and key end (kept so that advancing needs no loads within a segment).
 struct Cursor {
-  int si, ts;
+  int si, ts, b, ke;
 };
 __device__ __forceinline__ Cursor first_tile(const int32_t* segs, int si, int s_end) {
   for (; si < s_end; ++si) {
     const Seg s = load_seg(segs, si);
-    if (s.ke > s.ks) return Cursor{si, s.ks};
+    if (s.ke > s.ks) return Cursor{si, s.ks, s.b, s.ke};
   }
-  return Cursor{s_end, 0};
+  return Cursor{s_end, 0, 0, 0};
 }
 __device__ __forceinline__ Cursor next_tile(const int32_t* segs, Cursor c, int s_end) {
-  const Seg s = load_seg(segs, c.si);
-  if (c.ts + kTile < s.ke) return Cursor{c.si, c.ts + kTile};
+  if (c.ts + kTile < c.ke) return Cursor{c.si, c.ts + kTile, c.b, c.ke};
   return first_tile(segs, c.si + 1, s_end);
 }
 
@@ -192,84 +213,98 @@ __device__ __forceinline__ int64_t row_bytes(const DecodeArgs& a, const int32_t*
   return ((int64_t)page * a.s_page + (int64_t)((unsigned)j % ps) * a.s_tok) * esz;
 }
 
-// bf16: this wave's DMA of tile (b, keys ts..ts+31 clipped at ke) into `stage`: wave w
-// loads key rows 8w..8w+7, one instruction per latent row (lane = physical chunk) and
-// the rope parts of its 8 rows (lane = 8 rows x 8 chunks).
-template <bool PAGED32>
-__device__ __forceinline__ void issue_tile_bf16(const DecodeArgs& a, int b, int ts, int ke, uint32_t stage,
-                                                int w, int lane) {
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.bt_s;
-  const char* kvc = (const char*)a.kv_c;
-  const char* kpe = (const char*)a.k_pe;
-  const int kmax = ke - ts - 1;
-  const int64_t s_tok2 = a.s_tok * 2;
-  int64_t tile_base = 0;
-  if constexpr (PAGED32) tile_base = row_bytes(a, bt_row, ts, 2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int key = 8 * w + i;  // wave-uniform
-    const int kc = min(key, kmax);
-    const int64_t roff = PAGED32 ? tile_base + kc * s_tok2 : row_bytes(a, bt_row, ts + kc, 2);
-    dma16_s(kvc + roff, (uint32_t)((lane ^ lat_swz(key)) << 4),
-            __builtin_amdgcn_readfirstlane(stage + key * kLatRow));
-  }
-  // rope: lane = (row 8w + lane/8, physical chunk lane%8)
-  const int rk = 8 * w + (lane >> 3);
-  const uint32_t rlds = __builtin_amdgcn_readfirstlane(stage + kRopeOff + 8 * w * kRopeRow);
-  if constexpr (PAGED32) {
-    const int kc = min(rk, kmax);
-    const uint32_t voff = (uint32_t)(kc * s_tok2) + (((lane & 7) ^ rope_swz(rk)) << 4);
-    dma16_s(kpe + tile_base, voff, rlds);
-  } else {
-    // rows may sit on different pages: one instruction per row with only its 8 lanes active
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = 8 * w + i;
-      const int kc = min(key, kmax);
-      const int64_t roff = row_bytes(a, bt_row, ts + kc, 2);
-      if ((lane >> 3) == i) dma16_s(kpe + roff, (uint32_t)(((lane & 7) ^ rope_swz(key)) << 4), rlds);
-    }
-  }
+// Wave-uniform description of one tile's DMA.  With pages of a multiple of 32 keys the
+// tile sits in one page: one block_table lookup gives its base, then 32-bit offsets.
+struct DmaTile {
+  const char* kv;  // PAGED32: cache base + byte offset of the tile's first key; else cache base
+  const char* pe;
+  const int32_t* bt_row;
+  int ts, kmax;  // first key, last valid key offset within the tile
+  uint32_t lds;  // bf16 stage or raw fp8 stage
+};
+
+template <bool FP8, bool PAGED32>
+__device__ __forceinline__ DmaTile dma_tile(const DecodeArgs& a, const Cursor& pf, uint32_t lds) {
+  DmaTile t;
+  t.bt_row = a.block_table + (int64_t)pf.b * a.bt_s;
+  t.ts = pf.ts;
+  t.kmax = pf.ke - pf.ts - 1;
+  t.lds = lds;
+  const int64_t tb = PAGED32 ? row_bytes(a, t.bt_row, pf.ts, FP8 ? 1 : 2) : 0;
+  t.kv = (const char*)a.kv_c + tb;
+  t.pe = (const char*)a.k_pe + tb;
+  return t;
 }
 
-// fp8: this wave's DMA of the raw tile into a raw stage laid out as latent [32][512]
-// then rope [32][64] bytes, unswizzled.  Wave w loads keys 8w..8w+7: 4 latent
-// instructions of 2 keys each (lane = key half, 16-byte piece) and one rope
-// instruction on lanes 0..31 (lane = key 8w + lane/4, piece lane%4): 5 instructions.
-template <bool PAGED32>
-__device__ __forceinline__ void issue_tile_fp8(const DecodeArgs& a, int b, int ts, int ke, uint32_t raw,
-                                               int w, int lane) {
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.bt_s;
-  const char* kvc = (const char*)a.kv_c;
-  const char* kpe = (const char*)a.k_pe;
-  const int kmax = ke - ts - 1;
-  int64_t tile_base = 0;
-  if constexpr (PAGED32) tile_base = row_bytes(a, bt_row, ts, 1);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k0 = 8 * w + 2 * i;  // wave-uniform; this lane's key is k0 + lane/32
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(raw + k0 * kLkv);
-    if constexpr (PAGED32) {
-      const int kc = min(k0 + (lane >> 5), kmax);
-      dma16_s(kvc + tile_base, (uint32_t)(kc * a.s_tok) + 16 * (lane & 31), lds);
+// Number of dma_issue steps per tile (the DMA instruction count per wave is PER).
+template <bool FP8>
+constexpr int kDmaSteps = FP8 ? 5 : 9;
+
+// Step i of this wave's DMA of tile t.  Keys past the segment end load key kmax instead.
+// bf16: steps 0..7 load latent row 8w+i (lane = physical chunk), step 8 the rope parts of
+//   rows 8w..8w+7 (lane = 8 rows x 8 chunks; 8 row-wise instructions when rows may sit on
+//   different pages).
+// fp8 (raw stage: latent [32][512] then rope [32][64] bytes, unswizzled): steps 0..3 load
+//   latent rows 8w+2i, 8w+2i+1 (lane = key half, 16-byte piece), step 4 the rope parts of
+//   rows 8w..8w+7 on lanes 0..31 (lane = row 8w + lane/4, piece lane%4).
+template <bool FP8, bool PAGED32>
+__device__ __forceinline__ void dma_issue(const DecodeArgs& a, const DmaTile& t, int i, int w, int lane) {
+  if constexpr (!FP8) {
+    const uint32_t st = (uint32_t)a.s_tok * 2;
+    const uint32_t l16 = (uint32_t)lane << 4;
+    if (i < 8) {
+      const int key = 8 * w + i;  // wave-uniform
+      const int kc = min(key, t.kmax);
+      if constexpr (PAGED32) {
+        dma16_s(t.kv, (uint32_t)kc * st + (l16 ^ (uint32_t)(lat_swz(key) << 4)), t.lds + key * kLatRow);
+      } else {
+        dma16_s(t.kv + row_bytes(a, t.bt_row, t.ts + kc, 2), l16 ^ (uint32_t)(lat_swz(key) << 4),
+                t.lds + key * kLatRow);
+      }
     } else {
-      const int64_t r0 = row_bytes(a, bt_row, ts + min(k0, kmax), 1);
-      const int64_t r1 = row_bytes(a, bt_row, ts + min(k0 + 1, kmax), 1);
-      dma16(kvc + ((lane >> 5) ? r1 : r0) + 16 * (lane & 31), lds);
-    }
-  }
-  const uint32_t rlds = __builtin_amdgcn_readfirstlane(raw + kRawRopeOff + 8 * w * kRope);
-  if constexpr (PAGED32) {
-    const int kc = min(8 * w + (lane >> 2), kmax);
-    if (lane < 32) dma16_s(kpe + tile_base, (uint32_t)(kc * a.s_tok) + 16 * (lane & 3), rlds);
-  } else {
-    int64_t rb = 0;
+      const uint32_t rlds = t.lds + kRopeOff + 8 * w * kRopeRow;
+      if constexpr (PAGED32) {
+        const int rk = 8 * w + (lane >> 3);
+        const uint32_t kc = (uint32_t)min(rk, t.kmax);
+        dma16_s(t.pe, kc * st + ((((uint32_t)lane & 7) ^ (uint32_t)rope_swz(rk)) << 4), rlds);
+      } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = row_bytes(a, bt_row, ts + min(8 * w + i, kmax), 1);
-      if ((lane >> 2) == i) rb = r;
+        for (int r = 0; r < 8; ++r) {
+          const int key = 8 * w + r;
+          const int64_t roff = row_bytes(a, t.bt_row, t.ts + min(key, t.kmax), 2);
+          if ((lane >> 3) == r)
+            dma16_s(t.pe + roff, (((uint32_t)lane & 7) ^ (uint32_t)rope_swz(key)) << 4, rlds);
+        }
+      }
     }
-    if (lane < 32) dma16(kpe + rb + 16 * (lane & 3), rlds);
+  } else {
+    const uint32_t st = (uint32_t)a.s_tok;
+    if (i < 4) {
+      const int k0 = 8 * w + 2 * i;  // wave-uniform; this lane's key is k0 + lane/32
+      const uint32_t l16 = 16u * ((uint32_t)lane & 31);
+      if constexpr (PAGED32) {
+        const uint32_t kc = (uint32_t)min(k0 + (lane >> 5), t.kmax);
+        dma16_s(t.kv, kc * st + l16, t.lds + k0 * kLkv);
+      } else {
+        const int64_t r0 = row_bytes(a, t.bt_row, t.ts + min(k0, t.kmax), 1);
+        const int64_t r1 = row_bytes(a, t.bt_row, t.ts + min(k0 + 1, t.kmax), 1);
+        dma16(t.kv + ((lane >> 5) ? r1 : r0) + l16, t.lds + k0 * kLkv);
+      }
+    } else {
+      const uint32_t rlds = t.lds + kRawRopeOff + 8 * w * kRope;
+      if constexpr (PAGED32) {
+        const uint32_t kc = (uint32_t)min(8 * w + (lane >> 2), t.kmax);
+        if (lane < 32) dma16_s(t.pe, kc * st + 16u * ((uint32_t)lane & 3), rlds);
+      } else {
+        int64_t rb = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int64_t ro = row_bytes(a, t.bt_row, t.ts + min(8 * w + r, t.kmax), 1);
+          if ((lane >> 2) == r) rb = ro;
+        }
+        if (lane < 32) dma16(t.pe + rb + 16 * (lane & 3), rlds);
+      }
+    }
   }
 }
 
@@ -299,27 +334,31 @@ __device__ __forceinline__ u32x4_t read_vt(const char* p0, const char* p1) {
   return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
 }
 
-// Issues the next tile at the cursor, if any: DMA into the next bf16 stage or raw stage.
+// LDS target of the next tile to issue (bf16 stage or raw fp8 stage).
+template <bool FP8>
+__device__ __forceinline__ uint32_t next_lds(int issued) {
+  return FP8 ? lds_addr(smem + kRawOff) + (issued % kRawStages) * kRawBytes
+             : lds_addr(smem) + (issued % kStages) * kStageBytes;
+}
+
+// Issues the whole next tile at the cursor, if any (pipeline prologue).
 template <bool FP8, bool PAGED32>
 __device__ __forceinline__ void issue_next(const DecodeArgs& a, const int32_t* segs, int s_end, Cursor& pf,
                                            int& issued, int w) {
   if (pf.si >= s_end) return;
-  const Seg s = load_seg(segs, pf.si);
-  if constexpr (FP8)
-    issue_tile_fp8<PAGED32>(a, s.b, pf.ts, s.ke, lds_addr(smem + kRawOff) + (issued % kRawStages) * kRawBytes,
-                            w, lane_id());
-  else
-    issue_tile_bf16<PAGED32>(a, s.b, pf.ts, s.ke, lds_addr(smem) + (issued % kStages) * kStageBytes, w,
-                             lane_id());
+  const DmaTile t = dma_tile<FP8, PAGED32>(a, pf, next_lds<FP8>(issued));
+#pragma unroll
+  for (int i = 0; i < kDmaSteps<FP8>; ++i) dma_issue<FP8, PAGED32>(a, t, i, w, lane_id());
   pf = next_tile(segs, pf, s_end);
   issued++;
 }
 
 }  // namespace
 
-template <bool FP8, bool PAGED32>
+template <bool FP8, bool PAGED32, int NRB>
 __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
   constexpr int PER = FP8 ? 5 : (PAGED32 ? 9 : 16);  // DMA instructions per wave per tile
+  constexpr int NB = 4 * NRB;                          // accumulator blocks per wave
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
 
@@ -332,10 +371,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 
   const int R = a.Sq * a.N;
   const int row0 = hg * kGroupRows;
-  const int RG = min(kGroupRows, R - row0);  // rows of this group
-  const bool has_rows = 32 * w < RG;         // wave-uniform
+  const int RG = min(kGroupRows, R - row0);  // rows of this group, <= 32 NRB
+  const bool qk_wave = w < NRB;              // wave-uniform: owns query rows 32w..32w+31
   const int32_t* segs = a.segs;
   const int s_beg = ld_uniform(a.part_begin + part), s_end = ld_uniform(a.part_begin + part + 1);
+  float* fac_l = (float*)(smem + kFacOff);
+  float* ell_l = (float*)(smem + kEllOff);
 
   // ---- load pipeline (wave-uniform state) ----
   Cursor pf = first_tile(segs, s_beg, s_end);  // next tile to load
@@ -356,11 +397,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
     const int b = sg.b, ks = sg.ks, ke = sg.ke, pidx = sg.pidx;
     const int L = ld_uniform(a.seq_lens + b);
 
-    // Query rows of this wave: B operand of S^T = K . Q^T, 36 x 8 bf16 per lane
+    // Query rows of a QK wave: B operand of S^T = K . Q^T, 36 x 8 bf16 per lane
     // (lane: row 32w + l%32, dims 16k + 8(l/32) .. +7 of k-step k).
     u32x4_t qr[36];
     int lim = ke;  // keys j < lim are visible to this lane's row (segment end, causal window)
-    if (has_rows) {
+    if (qk_wave) {
       const int ql = lane_id(), rl = 32 * w + (ql & 31), qh = ql >> 5;
       if (rl < RG) {
         const int r = row0 + rl;
@@ -387,63 +428,90 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 
     float m_ref = -INFINITY;  // reference maximum of this lane's row (log2 units)
     float l_acc = 0.f;        // running sum over this lane's 16 keys of each tile
-    f32x16_t O[16];           // O^T[32 cols of block cb][32 rows], in AGPRs
-    acc_zero(O);
+    f32x16_t O[NB];           // O^T[32 cols of block cb][32 rows of block rb] at [cb * NRB + rb]
+    acc_zero<NB>(O);
 
     for (int ts = ks; ts < ke; ts += kTile) {
+      // ---- pipeline: wait for this tile, describe the next DMA, barrier ----
+      const bool do_dma = pf.si < s_end;  // wave-uniform
       const char* stage;
+      bool cvt_next = false;
       if constexpr (FP8) {
         // raw tile consumed+1 (if any) must have landed for every wave before it is widened
-        const bool next = consumed + 1 < issued;
-        if (next) wait_tiles<PER>(issued - consumed - 2);
-        barrier_lds();  // also: bf16 stage consumed%2 is complete, stage (consumed+1)%2 is free
-        issue_next<FP8, PAGED32>(a, segs, s_end, pf, issued, w);
-        if (next)
-          convert_fp8_tile(smem + kRawOff + ((consumed + 1) % kRawStages) * kRawBytes,
-                           smem + ((consumed + 1) & 1) * kStageBytes, 64 * w + lane_id());
+        cvt_next = consumed + 1 < issued;
+        if (cvt_next) wait_tiles<PER>(issued - consumed - 2);
         stage = smem + (consumed & 1) * kStageBytes;
       } else {
         wait_tiles<PER>(issued - consumed - 1);  // this wave's part of the tile has landed
-        barrier_lds();                           // ... every wave's; stage consumed-1 is free
-        issue_next<FP8, PAGED32>(a, segs, s_end, pf, issued, w);
         stage = smem + (consumed % kStages) * kStageBytes;
       }
+      DmaTile dt{};
+      if (do_dma) dt = dma_tile<FP8, PAGED32>(a, pf, next_lds<FP8>(issued));
+      // every wave's part has landed; the stage issued into next and P are free
+      barrier_lds();
+      if constexpr (FP8) {
+        if (cvt_next)
+          convert_fp8_tile(smem + kRawOff + ((consumed + 1) % kRawStages) * kRawBytes,
+                           smem + ((consumed + 1) & 1) * kStageBytes, 64 * w + lane_id());
+      }
 
-      if (has_rows) {
+      // V^T fragments of this wave's columns for both k-steps (see the PV step below).
+      // Requested before the softmax so that they arrive while it runs.
+      u32x4_t vt[2][4];
+      auto load_vt = [&]() {
+        const int pl = lane_id(), ph = pl >> 5, g = pl >> 4, j = pl & 15;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          int off[2];
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const int key = 4 * ph + (j >> 2) + 8 * kh;
+            const int col = 128 * w + 32 * cb + 16 * (g & 1) + 4 * (j & 3);
+            off[kh] = key * kLatRow + (((col >> 3) ^ lat_swz(key)) << 4) + 8 * ((col >> 2) & 1);
+          }
+#pragma unroll
+          for (int sk = 0; sk < 2; ++sk)
+            vt[sk][cb] = read_vt(stage + off[0] + 16 * kLatRow * sk, stage + off[1] + 16 * kLatRow * sk);
+        }
+      };
+
+      if (qk_wave) {
         // ---- S^T[32 keys][32 rows] = K . Q^T: 36 k-steps over the 576 dims ----
         // A operand: key r32, logical chunk 2k + h2 at kq_off[k & 7] + 256 (k >> 3)
         // (latent, k < 32; the swizzle permutes chunks within a 16-chunk group) or
-        // kr_off[k - 32] (rope).  K fragments stream through a 4-deep ring.
+        // kr_off[k - 32] (rope).  K fragments stream through an 8-deep ring; the DMA of
+        // the next tile is spread over the chain, one step after every fourth MFMA.
         f32x16_t sacc;
-        int h2;
+        const int ln = lane_id(), r32 = ln & 31, h2 = ln >> 5;
         {
-          const int ln = lane_id(), r32 = ln & 31;
-          h2 = ln >> 5;
           int kq_off[8], kr_off[4];
 #pragma unroll
           for (int m = 0; m < 8; ++m) kq_off[m] = r32 * kLatRow + (((2 * m + h2) ^ lat_swz(r32)) << 4);
 #pragma unroll
           for (int m = 0; m < 4; ++m)
             kr_off[m] = kRopeOff + r32 * kRopeRow + (((2 * m + h2) ^ rope_swz(r32)) << 4);
-          u32x4_t kb[4];
+          auto k_at = [&](int k) {
+            return *(const u32x4_t*)(stage + (k < 32 ? kq_off[k & 7] + 256 * (k >> 3) : kr_off[k - 32]));
+          };
+          u32x4_t kb[8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) kb[k] = *(const u32x4_t*)(stage + kq_off[k]);
+          for (int k = 0; k < 8; ++k) kb[k] = k_at(k);
 #pragma unroll
           for (int k = 0; k < 36; ++k) {
             if (k == 0)
               mfma_first(sacc, kb[0], qr[0]);
             else if (k == 35)
-              mfma_acc_v_last(sacc, kb[k & 3], qr[k]);
+              mfma_acc_v_last(sacc, kb[k & 7], qr[k]);
             else
-              mfma_acc_v(sacc, kb[k & 3], qr[k]);
-            const int kn = k + 4;
-            if (kn < 36)
-              kb[k & 3] =
-                  *(const u32x4_t*)(stage + (kn < 32 ? kq_off[kn & 7] + 256 * (kn >> 3) : kr_off[kn - 32]));
+              mfma_acc_v(sacc, kb[k & 7], qr[k]);
+            if (k + 8 < 36) kb[k & 7] = k_at(k + 8);
+            if ((k & 3) == 3 && (k >> 2) < kDmaSteps<FP8> && do_dma)
+              dma_issue<FP8, PAGED32>(a, dt, k >> 2, w, lane_id());
           }
         }
+        load_vt();
 
-        // ---- softmax (lane: row l%32, keys ts + 8(v/4) + 4 h2 + v%4) ----
+        // ---- softmax (lane: row 32w + l%32, keys ts + 8(v/4) + 4 h2 + v%4) ----
         const float c = a.qk_scale_log2;
         if (!__all(ts + kTile <= lim)) {
           const int rem = lim - ts - 4 * h2;
@@ -455,20 +523,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
         mx = half_max(mx) * c;
+        float fac = 1.f;  // factor for this row's O and sum (applied by every wave)
         if (__any(mx > m_ref + kRescaleAt)) {
           if (__all(m_ref == -INFINITY)) {
             m_ref = mx;  // first keys of the segment: O and the sums are still zero
           } else {
             const float m_new = fmaxf(m_ref, mx);
-            const float f = (m_new > m_ref) ? fast_exp2(m_ref - m_new) : 1.f;
-            l_acc *= f;
-#pragma unroll
-            for (int cb = 0; cb < 16; ++cb) {
-              acc_fence(O[cb]);
-#pragma unroll
-              for (int v = 0; v < 16; ++v) O[cb][v] *= f;
-              acc_written(O[cb]);
-            }
+            fac = (m_new > m_ref) ? fast_exp2(m_ref - m_new) : 1.f;
+            l_acc *= fac;
             m_ref = m_new;
           }
         }
@@ -484,84 +546,128 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
           pk[v >> 1] = pack_bf16x2(p0, p1);
         }
         l_acc += psum;
+        // P chunk q = 2s + h2 of row 32w + r32 holds keys 16s + 4 h2 + (e & 3) + 8 (e >> 2)
+        const int prow = 32 * w + r32;
+        *(u32x4_t*)(smem + p_off(prow, h2)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+        *(u32x4_t*)(smem + p_off(prow, 2 + h2)) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
+        if (h2 == 0) fac_l[prow] = fac;
+      } else {
+        if (do_dma) {
+#pragma unroll
+          for (int i = 0; i < kDmaSteps<FP8>; ++i) dma_issue<FP8, PAGED32>(a, dt, i, w, lane_id());
+        }
+        load_vt();
+      }
+      if (do_dma) {
+        pf = next_tile(segs, pf, s_end);
+        issued++;
+      }
+      barrier_lds();  // P and the factors of every row are in LDS
 
-        // ---- O^T[32 cols][32 rows] += V^T . P^T per column block, 16 keys per k-step ----
-        // B operand: P^T keys 16s + 4 h2 + (e & 3) + 8 (e >> 2), e = 0..7, which are
-        // elements 8s..8s+7 of this lane's S^T accumulator.  A operand: V^T through
-        // ds_read_b64_tr_b16: 16-lane group g covers columns 32cb + 16(g & 1) + 0..15 and
-        // keys t0..t0+3 (t0 = 16s + 4(g >> 1), +8 for the second read); lane j addresses
-        // key t0 + j/4 at columns +4(j & 3) and receives keys t0..t0+3 of column +j.
-        {
-          const int pl = lane_id(), ph = pl >> 5, g = pl >> 4, j = pl & 15;
-          int vt_off[2][4];  // [key half][cb & 3]; + 256 (cb >> 2) + 16 KB s
+      // ---- rescale (rare): O rows whose reference maximum was raised this tile ----
+      {
+        const int fl = lane_id() & 31;
+        float f[NRB];
+        bool any = false;
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            const int key = 4 * ph + (j >> 2) + 8 * kh;
+        for (int rb = 0; rb < NRB; ++rb) {
+          f[rb] = fac_l[32 * rb + fl];
+          any |= f[rb] != 1.f;
+        }
+        if (__any(any)) {
 #pragma unroll
-            for (int cq = 0; cq < 4; ++cq) {
-              const int col = 32 * cq + 16 * (g & 1) + 4 * (j & 3);
-              vt_off[kh][cq] = key * kLatRow + (((col >> 3) ^ lat_swz(key)) << 4) + 8 * ((col >> 2) & 1);
-            }
-          }
-          auto vt_at = [&](int i) {  // V^T fragment i = 16 s + cb
-            const int o = 256 * ((i & 15) >> 2) + 16 * kLatRow * (i >> 4);
-            return read_vt(stage + vt_off[0][i & 3] + o, stage + vt_off[1][i & 3] + o);
-          };
-          // fragments stream through a 4-deep ring: MFMA i, then load fragment i + 4
-          u32x4_t vb[4];
+          for (int i = 0; i < NB; ++i) {
+            acc_fence(O[i]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vb[i] = vt_at(i);
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const int s = i >> 4, cb = i & 15;
-            const u32x4_t pf4 = u32x4_t{pk[4 * s], pk[4 * s + 1], pk[4 * s + 2], pk[4 * s + 3]};
-            if (i == 31)
-              mfma_acc_a_last(O[cb], vb[i & 3], pf4);
-            else
-              mfma_acc_a(O[cb], vb[i & 3], pf4);
-            if (i + 4 < 32) vb[i & 3] = vt_at(i + 4);
+            for (int v = 0; v < 16; ++v) O[i][v] *= f[i % NRB];
+            acc_written(O[i]);
           }
         }
+      }
+
+      // ---- O^T[cols 128w + 32cb ..][rows 32rb ..] += V^T . P^T, 16 keys per k-step ----
+      // B operand (P^T): row 32rb + l%32, logical keys 8(l/32) + e of k-step s = chunk
+      // 2s + l/32 of the P row.  A operand (V^T) through ds_read_b64_tr_b16: 16-lane
+      // group g covers columns 128w + 32cb + 16(g & 1) + 0..15 and keys t0..t0+3
+      // (t0 = 16s + 4(g >> 1), +8 for the second read); lane j addresses key t0 + j/4 at
+      // columns +4(j & 3) and receives keys t0..t0+3 of column +j.
+      {
+        const int pl = lane_id(), p32 = pl & 31, ph = pl >> 5;
+        u32x4_t pf4[2][NRB];
+#pragma unroll
+        for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            pf4[sk][rb] = *(const u32x4_t*)(smem + p_off(32 * rb + p32, 2 * sk + ph));
+#pragma unroll
+        for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+              if (sk == 1 && cb == 3 && rb == NRB - 1)
+                mfma_acc_a_last(O[cb * NRB + rb], vt[sk][cb], pf4[sk][rb]);
+              else
+                mfma_acc_a(O[cb * NRB + rb], vt[sk][cb], pf4[sk][rb]);
+            }
       }
       consumed++;
     }
 
     // ---- epilogue: o = O * kv_scale / l, lse = ln(sum exp) ----
-    if (has_rows) {
+    if (qk_wave) {
       const float l_row = half_sum(l_acc);
-      const int el = lane_id(), eh = el >> 5;
+      const int el = lane_id();
       const int rl = 32 * w + (el & 31);
-      if (rl < RG) {
+      if (el < 32) ell_l[rl] = l_row;
+      if (el < 32 && rl < RG) {
         const int r = row0 + rl;
         const float lse = (l_row > 0.f) ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
-        const float f = (l_row > 0.f) ? a.out_scale / l_row : 0.f;
         const int t = r / a.N, h = r - t * a.N;
         if (pidx < 0) {
-          if (a.lse && eh == 0) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
+          if (a.lse) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
+        } else {
+          a.ws_lse[(int64_t)pidx * R + r] = lse;
+        }
+      }
+    }
+    barrier_lds();  // row sums of every row are in LDS
+    {
+      const int el = lane_id(), e32 = el & 31, eh = el >> 5;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int rl = 32 * rb + e32;
+        if (rl >= RG) continue;
+        const int r = row0 + rl;
+        const float lsum = ell_l[rl];
+        const float f = (lsum > 0.f) ? a.out_scale / lsum : 0.f;
+        const int t = r / a.N, h = r - t * a.N;
+        if (pidx < 0) {
           uint16_t* orow = a.o + ((int64_t)b * a.Sq + t) * a.o_s_tok + (int64_t)h * a.o_s_head;
 #pragma unroll
-          for (int cb = 0; cb < 16; ++cb) {
-            acc_fence(O[cb]);
+          for (int cb = 0; cb < 4; ++cb) {
+            f32x16_t& acc = O[cb * NRB + rb];
+            acc_fence(acc);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int col = 32 * cb + 8 * gq + 4 * eh;
+              const int col = 128 * w + 32 * cb + 8 * gq + 4 * eh;
               u32x2_t pk2;
-              pk2[0] = pack_bf16x2(O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f);
-              pk2[1] = pack_bf16x2(O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f);
+              pk2[0] = pack_bf16x2(acc[4 * gq] * f, acc[4 * gq + 1] * f);
+              pk2[1] = pack_bf16x2(acc[4 * gq + 2] * f, acc[4 * gq + 3] * f);
               *(u32x2_t*)(orow + col) = pk2;
             }
           }
         } else {
-          if (eh == 0) a.ws_lse[(int64_t)pidx * R + r] = lse;
           float* prow = a.ws_o + ((int64_t)pidx * R + r) * kLkv;
 #pragma unroll
-          for (int cb = 0; cb < 16; ++cb) {
-            acc_fence(O[cb]);
+          for (int cb = 0; cb < 4; ++cb) {
+            f32x16_t& acc = O[cb * NRB + rb];
+            acc_fence(acc);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int col = 32 * cb + 8 * gq + 4 * eh;
-              *(f32x4_t*)(prow + col) = f32x4_t{O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f,
-                                                O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f};
+              const int col = 128 * w + 32 * cb + 8 * gq + 4 * eh;
+              *(f32x4_t*)(prow + col) =
+                  f32x4_t{acc[4 * gq] * f, acc[4 * gq + 1] * f, acc[4 * gq + 2] * f, acc[4 * gq + 3] * f};
             }
           }
         }
@@ -571,16 +677,29 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
   wait_vm<0>();  // no DMA outlives the workgroup
 }
 
+template <bool FP8, bool PAGED32>
+static void launch_nrb(const DecodeArgs& a, int nrb, dim3 grid, hipStream_t stream) {
+  switch (nrb) {
+    case 1: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 1>), grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 2>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 4>), grid, dim3(256), 0, stream, a); break;
+  }
+}
+
 hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
+  // Every head group but the last has 128 rows; the last may be smaller, but a group
+  // never needs more row blocks than the first one, so one instance serves all.
+  const int R = a.Sq * a.N;
+  const int nrb = (min(R, kGroupRows) + 31) / 32;
   const int parts8 = (a.num_parts + 7) / 8 * 8;
   const dim3 grid(parts8 * a.head_groups);
   const bool p32 = (a.page_size % 32) == 0;
   if (fp8) {
-    if (p32) hipLaunchKernelGGL((mla_decode_kernel<true, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_kernel<true, false>), grid, dim3(256), 0, stream, a);
+    if (p32) launch_nrb<true, true>(a, nrb, grid, stream);
+    else launch_nrb<true, false>(a, nrb, grid, stream);
   } else {
-    if (p32) hipLaunchKernelGGL((mla_decode_kernel<false, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_kernel<false, false>), grid, dim3(256), 0, stream, a);
+    if (p32) launch_nrb<false, true>(a, nrb, grid, stream);
+    else launch_nrb<false, false>(a, nrb, grid, stream);
   }
   return hipGetLastError();
 }
