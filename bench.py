@@ -12,8 +12,15 @@ dominant kernel (the decode kernel, timed with HIP events on the stream it is
 launched on) and the CPU fp64 oracle timed on a bounded sample of the same batch.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3|longtail|verify|fp8|tiny]
+  python bench.py --calibrate-copy     # a plain device copy of known size, for counter scaling
+
+roofline.traffic is the decode kernel's HBM bytes per launch from rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters (profiles/traffic_<workload>.txt), each scaled by what the same counter
+reads for the copy of known size; it is null when that record was taken on other kernel
+sources than the ones built now.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +38,52 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 LKV, ROPE = 512, 64
 WANT_LSE = {"tiny": True, "dsv3": False, "longtail": False, "verify": False, "fp8": True}
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("decode.hip", "common.h", "kernels.h", "plan.h")
+COPY_BYTES = 1 << 30  # calibration copy: reads and writes this many bytes
+
+
+def kernel_digest():
+    """sha256 over the sources the decode kernel is built from."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mla_paged_decode_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per decode launch from the committed counter record, or None when the record
+    is missing or was taken on other kernel sources.  Record lines are `key: value`."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                rec[k.strip()] = v.strip()
+    try:
+        if rec.get("kernel_sources_sha256") != kernel_digest():
+            return None
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(steps):
+    """A device-to-device copy of COPY_BYTES, the known-size reference for the counters."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_read": COPY_BYTES, "calibration_copy_bytes_written": COPY_BYTES,
+                      "launches": steps}), flush=True)
 
 
 def algorithmic_work(w, seq_lens, with_lse):
@@ -107,11 +160,16 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20)
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (no collectives); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(max(1, min(args.steps, 5)))
+        return
 
     import torch
     from mla_paged_decode_03_amd import api
@@ -201,12 +259,13 @@ def main():
     tflops = work_alg["flops"] / (dec_us * 1e-6) / 1e12
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "hbm" if work_alg["flops"] / work_alg["bytes"] < ridge else "mfma"
+    traffic = load_traffic(w.name)
     if bound == "hbm":
         roof = dict(bound="hbm", achieved=round(hbm_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(hbm_gbs / HBM_PEAK_GBS, 4), traffic=None)
+                    frac=round(hbm_gbs / HBM_PEAK_GBS, 4), traffic=traffic)
     else:
         roof = dict(bound="mfma", achieved=round(tflops, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tflops / BF16_PEAK_TFLOPS, 4), traffic=None)
+                    frac=round(tflops / BF16_PEAK_TFLOPS, 4), traffic=traffic)
     t_roof_us = max(work_alg["bytes"] / (HBM_PEAK_GBS * 1e9), work_alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
 
     tokens_per_s = T / (ms_per_step * 1e-3)
@@ -230,6 +289,7 @@ def main():
         "plan": {"parts": int(work[:, 0].max()) + 1 if len(work) else 0, "segments": int(len(work)),
                  "split_requests": int(len(red)), "workspace_bytes": int(plan.workspace_bytes)},
         "input_gen_s": round(t_gen, 2),
+        "kernel_sources_sha256": kernel_digest(),
     }
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
