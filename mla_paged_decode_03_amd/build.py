@@ -19,7 +19,7 @@ CLANGXX = "/opt/rocm/lib/llvm/bin/clang++"
 ARCH = "gfx950"
 
 COMMON = [
-    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
     # Packed fp32 VALU ops stay off: the compiler must not form v_pk_*_f32.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -39,6 +39,8 @@
 // asm, so each statement carries its own wait states: 3 before an MFMA whose
 // operands a VALU may just have written, 16 after the last MFMA of a chain whose
 // result is read next (the compiler itself pads 1-2 and 12 on gfx950).
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -677,6 +679,306 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
   wait_vm<0>();  // no DMA outlives the workgroup
 }
 
+// ---------------------------------------------------------------------------------
+// Software-pipelined variant for bf16 caches (one barrier per step).  Wave w owns query
+// rows 32w..32w+31 from end to end, with O (all 512 columns) in the 256 AGPRs and P in
+// VGPRs, so nothing but the key tile is shared.  Step s of a segment runs the 36 QK
+// MFMAs of tile q (with the DMA of a later tile between them), then the 32 P.V MFMAs
+// of tile q-1 with the softmax of tile q between them, so the MFMA pipe keeps working
+// through the VALU work.  A segment of n tiles takes n + 1 steps (no P.V in the
+// first, no QK in the last).  A stage is reloaded only after the P.V of the tile it
+// held, so up to two tiles are in flight beyond the two in use.
+// ---------------------------------------------------------------------------------
+
+// Calls f(std::integral_constant<int, K>) for K = 0..N-1 in order, as straight-line code.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... K>(std::integer_sequence<int, K...>) {
+    (f(std::integral_constant<int, K>{}), ...);
+  }(std::make_integer_sequence<int, N>{});
+}
+
+// Marks a value as (re)defined here: work that uses it cannot move above this point.
+template <typename T>
+__device__ __forceinline__ void redef(T& x) { asm volatile("" : "+v"(x)); }
+// Marks a value as used here: the work producing it cannot move below this point.
+template <typename T>
+__device__ __forceinline__ void use(const T& x) { asm volatile("" ::"v"(x)); }
+
+template <bool PAGED32>
+__global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
+  constexpr int PER = PAGED32 ? 9 : 16;  // DMA instructions per wave per tile
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
+
+  // Workgroups are dealt round-robin to the 8 XCDs; keep the head groups of
+  // one part on one XCD so that they share its L2 for the part's keys.
+  const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
+  const int hg = slot % a.head_groups;
+  const int part = xcd + 8 * (slot / a.head_groups);
+  if (part >= a.num_parts) return;
+
+  const int R = a.Sq * a.N;
+  const int row0 = hg * kGroupRows;
+  const int RG = min(kGroupRows, R - row0);  // rows of this group
+  const bool has_rows = 32 * w < RG;         // wave-uniform
+  const int32_t* segs = a.segs;
+  const int s_beg = ld_uniform(a.part_begin + part), s_end = ld_uniform(a.part_begin + part + 1);
+  const float c = a.qk_scale_log2;
+
+  Cursor pf = first_tile(segs, s_beg, s_end);  // next tile to load
+  int issued = 0, tq = 0;                      // tiles issued; tiles whose QK has run
+#pragma unroll 1
+  for (int k = 0; k < kStages; ++k) issue_next<false, PAGED32>(a, segs, s_end, pf, issued, w);
+
+  for (int si = s_beg; si < s_end; ++si) {
+    const Seg sg = load_seg(segs, si);
+    const int b = sg.b, ks = sg.ks, ke = sg.ke, pidx = sg.pidx;
+    const int L = ld_uniform(a.seq_lens + b);
+
+    // Query rows of this wave: B operand of S^T = K . Q^T, 36 x 8 bf16 per lane
+    // (lane: row 32w + l%32, dims 16k + 8(l/32) .. +7 of k-step k).
+    u32x4_t qr[36];
+    int lim = ke;  // keys j < lim are visible to this lane's row (segment end, causal window)
+    if (has_rows) {
+      const int ql = lane_id(), rl = 32 * w + (ql & 31), qh = ql >> 5;
+      if (rl < RG) {
+        const int r = row0 + rl;
+        const int t = r / a.N, h = r - t * a.N;
+        const int64_t tok = (int64_t)b * a.Sq + t;
+        const uint16_t* qn = a.q_nope + tok * a.q_nope_s_tok + (int64_t)h * a.q_nope_s_head + 8 * qh;
+        const uint16_t* qp = a.q_pe + tok * a.q_pe_s_tok + (int64_t)h * a.q_pe_s_head + 8 * qh;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) qr[k] = *(const u32x4_t*)(qn + 16 * k);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qr[32 + k] = *(const u32x4_t*)(qp + 16 * k);
+        lim = min(ke, L - (a.Sq - 1) + t);
+      } else {
+        // padding rows: zero queries give zero logits; their probabilities only reach
+        // output rows that are never stored
+#pragma unroll
+        for (int k = 0; k < 36; ++k) qr[k] = u32x4_t{0, 0, 0, 0};
+      }
+      // A wait the compiler sees: the query loads are complete before the tile loop,
+      // so it places no vmcnt waits there (those would also count the DMA loads in
+      // flight and drain the prefetch pipeline).  s_waitcnt vmcnt(0).
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+
+    float m_ref = -INFINITY;  // reference maximum of this lane's row (log2 units)
+    float l_acc = 0.f;        // running sum over this lane's 16 keys of each tile
+    f32x16_t O[16];           // O^T[32 cols of block cb][32 rows], in AGPRs
+    acc_zero<16>(O);
+    uint32_t pkp[8];          // P of the previous tile: bf16 pairs, B operand of its P.V
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pkp[i] = 0;
+
+    const int nt = (ke - ks + kTile - 1) / kTile;
+    for (int st = 0; st < nt + (nt > 0 ? 1 : 0); ++st) {
+      const bool do_qk = st < nt, do_pv = st > 0;  // wave-uniform
+      if (do_qk) wait_tiles<PER>(issued - tq - 1);  // this wave's part of tile tq has landed
+      const int pv_done = tq - (do_pv ? 1 : 0);     // tiles whose P.V is complete
+      const bool do_dma = pf.si < s_end && issued < pv_done + kStages;
+      DmaTile dt{};
+      if (do_dma) dt = dma_tile<false, PAGED32>(a, pf, next_lds<false>(issued));
+      barrier_lds();  // tile tq has landed for every wave; the stage of tile tq-2 is free
+      const char* qst = smem + (tq % kStages) * kStageBytes;
+      const char* pst = smem + ((tq + kStages - 1) % kStages) * kStageBytes;
+      const int ts = ks + kTile * st;  // first key of tile tq
+
+      if (has_rows) {
+        const int ln = lane_id(), r32 = ln & 31, h2 = ln >> 5;
+        f32x16_t sc;
+        if (do_qk) {
+          // ---- S^T[32 keys][32 rows] = K . Q^T: 36 k-steps over the 576 dims ----
+          // A operand: key r32, logical chunk 2k + h2 = (2k) ^ h2, so its swizzled chunk
+          // is (2k) ^ (h2 ^ swz).  K fragments stream through a ring; one DMA step of a
+          // later tile follows every second MFMA from the fourth on.
+          const int kx = h2 ^ lat_swz(r32), rx = h2 ^ rope_swz(r32);
+          const char* kbase = qst + r32 * kLatRow;
+          const char* rbase = qst + kRopeOff + r32 * kRopeRow;
+          auto k_at = [&](int k) __attribute__((always_inline)) {
+            return k < 32 ? *(const u32x4_t*)(kbase + (((2 * (k & 7)) ^ kx) << 4) + 256 * (k >> 3))
+                          : *(const u32x4_t*)(rbase + (((2 * (k - 32)) ^ rx) << 4));
+          };
+          constexpr int KR = 6;  // K fragment ring depth
+          u32x4_t kb[KR];
+#pragma unroll
+          for (int k = 0; k < KR; ++k) kb[k] = k_at(k);
+          static_for<36>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            if constexpr (k == 0)
+              mfma_first(sc, kb[0], qr[0]);
+            else if constexpr (k == 35)
+              mfma_acc_v_last(sc, kb[k % KR], qr[k]);
+            else
+              mfma_acc_v(sc, kb[k % KR], qr[k]);
+            if constexpr (k + KR < 36) kb[k % KR] = k_at(k + KR);
+            if constexpr (k >= 3 && (k - 3) % 2 == 0 && (k - 3) / 2 < kDmaSteps<false>) {
+              if (do_dma) dma_issue<false, PAGED32>(a, dt, (k - 3) / 2, w, lane_id());
+            }
+          });
+        } else if (do_dma) {
+#pragma unroll
+          for (int i = 0; i < kDmaSteps<false>; ++i) dma_issue<false, PAGED32>(a, dt, i, w, lane_id());
+        }
+
+        // ---- softmax of tile tq in chunks (lane: row 32w + r32, keys ts + 8(v/4) + 4 h2
+        // + v%4), branch-free so that they stay between the P.V MFMAs ----
+        float mx = 0.f, fac = 1.f, nm = 0.f, psum = 0.f;
+        uint32_t pkn[8];
+        auto soft = [&](auto chc) __attribute__((always_inline)) {
+          constexpr int ch = decltype(chc)::value;
+          if constexpr (ch == 0) {
+            redef(sc);
+            const int rem = lim - ts - 4 * h2;  // key offset 8(v/4) + v%4 is visible iff < rem
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (8 * (v >> 2) + (v & 3) >= rem) sc[v] = -INFINITY;
+            mx = sc[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+            use(mx);
+          } else if constexpr (ch == 1) {
+            redef(mx);
+            mx = half_max(mx) * c;
+            // raise the reference when a tile exceeds it by more than 2^8 (the first tile
+            // with visible keys raises it from -inf, with nothing to rescale yet)
+            const bool need = __any(mx > m_ref + kRescaleAt);
+            const float m_new = need ? fmaxf(m_ref, mx) : m_ref;
+            fac = (m_new > m_ref && m_ref != -INFINITY) ? fast_exp2(m_ref - m_new) : 1.f;
+            l_acc *= fac;
+            m_ref = m_new;
+            // exp2(-inf) = 0 covers masked keys; rows without a visible key keep m = -inf
+            nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
+            use(nm);
+          } else if constexpr (ch < 10) {
+            constexpr int v = 2 * (ch - 2);
+            redef(nm);
+            const float p0 = fast_exp2(fmaf(sc[v], c, nm));
+            const float p1 = fast_exp2(fmaf(sc[v + 1], c, nm));
+            psum += p0 + p1;
+            pkn[v >> 1] = pack_bf16x2(p0, p1);
+            use(pkn[v >> 1]);
+          } else {
+            l_acc += psum;
+          }
+        };
+
+        if (do_pv) {
+          // ---- O^T[32 cols][32 rows] += V^T . P^T of tile tq-1, 16 keys per k-step ----
+          // B operand: P^T keys 16s + 4 h2 + (e & 3) + 8 (e >> 2), e = 0..7, which are
+          // elements 8s..8s+7 of this lane's S^T accumulator.  A operand: V^T through
+          // ds_read_b64_tr_b16: 16-lane group g covers columns 32cb + 16(g & 1) + 0..15
+          // and keys t0..t0+3 (t0 = 16s + 4(g >> 1), +8 for the second read); lane j
+          // addresses key t0 + j/4 at columns +4(j & 3) and receives keys t0..t0+3 of
+          // column +j.  Fragments stream through a 4-deep ring.
+          const int g = ln >> 4, j = ln & 15;
+          int vt_off[2][4];  // [key half][cb & 3]; + 256 (cb >> 2) + 16 KB s
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const int key = 4 * h2 + (j >> 2) + 8 * kh;
+#pragma unroll
+            for (int cq = 0; cq < 4; ++cq) {
+              const int col = 32 * cq + 16 * (g & 1) + 4 * (j & 3);
+              vt_off[kh][cq] = key * kLatRow + (((col >> 3) ^ lat_swz(key)) << 4) + 8 * ((col >> 2) & 1);
+            }
+          }
+          auto vt_at = [&](int i) __attribute__((always_inline)) {  // fragment i = 16 s + cb
+            const int o = 256 * ((i & 15) >> 2) + 16 * kLatRow * (i >> 4);
+            return read_vt(pst + vt_off[0][i & 3] + o, pst + vt_off[1][i & 3] + o);
+          };
+          u32x4_t vb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vb[i] = vt_at(i);
+          static_for<32>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int sk = i >> 4, cb = i & 15;
+            const u32x4_t pf4 = u32x4_t{pkp[4 * sk], pkp[4 * sk + 1], pkp[4 * sk + 2], pkp[4 * sk + 3]};
+            if constexpr (i == 31)
+              mfma_acc_a_last(O[cb], vb[i & 3], pf4);
+            else
+              mfma_acc_a(O[cb], vb[i & 3], pf4);
+            if constexpr (i + 4 < 32) vb[i & 3] = vt_at(i + 4);
+            if constexpr (i >= 1 && i - 1 <= 10) {
+              if (do_qk) soft(std::integral_constant<int, i - 1>{});
+            }
+          });
+        } else {
+          static_for<11>([&](auto chc) __attribute__((always_inline)) { soft(chc); });
+        }
+
+        if (do_qk) {
+          // rare: O rows whose reference maximum was raised by tile tq (O holds P.V up to
+          // tile tq-1, taken against the old reference)
+          if (__any(fac != 1.f)) {
+#pragma unroll
+            for (int cb = 0; cb < 16; ++cb) {
+              acc_fence(O[cb]);
+#pragma unroll
+              for (int v = 0; v < 16; ++v) O[cb][v] *= fac;
+              acc_written(O[cb]);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pkp[i] = pkn[i];
+        }
+      } else if (do_dma) {
+#pragma unroll
+        for (int i = 0; i < kDmaSteps<false>; ++i) dma_issue<false, PAGED32>(a, dt, i, w, lane_id());
+      }
+      if (do_dma) {
+        pf = next_tile(segs, pf, s_end);
+        issued++;
+      }
+      if (do_qk) tq++;
+    }
+
+    // ---- epilogue: o = O * kv_scale / l, lse = ln(sum exp) ----
+    if (has_rows) {
+      const float l_row = half_sum(l_acc);
+      const int el = lane_id(), eh = el >> 5;
+      const int rl = 32 * w + (el & 31);
+      if (rl < RG) {
+        const int r = row0 + rl;
+        const float lse = (l_row > 0.f) ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
+        const float f = (l_row > 0.f) ? a.out_scale / l_row : 0.f;
+        const int t = r / a.N, h = r - t * a.N;
+        if (pidx < 0) {
+          if (a.lse && eh == 0) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
+          uint16_t* orow = a.o + ((int64_t)b * a.Sq + t) * a.o_s_tok + (int64_t)h * a.o_s_head;
+#pragma unroll
+          for (int cb = 0; cb < 16; ++cb) {
+            acc_fence(O[cb]);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = 32 * cb + 8 * gq + 4 * eh;
+              u32x2_t pk2;
+              pk2[0] = pack_bf16x2(O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f);
+              pk2[1] = pack_bf16x2(O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f);
+              *(u32x2_t*)(orow + col) = pk2;
+            }
+          }
+        } else {
+          if (eh == 0) a.ws_lse[(int64_t)pidx * R + r] = lse;
+          float* prow = a.ws_o + ((int64_t)pidx * R + r) * kLkv;
+#pragma unroll
+          for (int cb = 0; cb < 16; ++cb) {
+            acc_fence(O[cb]);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = 32 * cb + 8 * gq + 4 * eh;
+              *(f32x4_t*)(prow + col) = f32x4_t{O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f,
+                                                O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f};
+            }
+          }
+        }
+      }
+    }
+  }
+  wait_vm<0>();  // no DMA outlives the workgroup
+}
+
 template <bool FP8, bool PAGED32>
 static void launch_nrb(const DecodeArgs& a, int nrb, dim3 grid, hipStream_t stream) {
   switch (nrb) {
@@ -698,8 +1000,8 @@ hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
     if (p32) launch_nrb<true, true>(a, nrb, grid, stream);
     else launch_nrb<true, false>(a, nrb, grid, stream);
   } else {
-    if (p32) launch_nrb<false, true>(a, nrb, grid, stream);
-    else launch_nrb<false, false>(a, nrb, grid, stream);
+    if (p32) hipLaunchKernelGGL((mla_decode_pipe_kernel<true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_pipe_kernel<false>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
