@@ -125,7 +125,7 @@ int mla_decode_plan(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t
   p->seq_lens.assign(seq_lens_host, seq_lens_host + B);
   p->stream = (hipStream_t)stream;
   p->device = device;
-  p->ws_bytes = (size_t)p->host.num_partials * Sq * N * (mla::kLkv * 4 + 4);
+  p->ws_bytes = (size_t)p->host.num_partials * ((size_t)mla::partial_rows(Sq, N) * mla::kLkv * 4 + (size_t)Sq * N * 4);
 
   const size_t nseg = p->host.segs.size();
   p->off_part = 4 * nseg;
@@ -263,7 +263,9 @@ int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, i
   a.lse = lse;
   const size_t R = (size_t)hp.Sq * hp.N;
   a.ws_o = (float*)workspace;
-  a.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * R * mla::kLkv * 4) : nullptr;
+  a.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * mla::partial_rows(hp.Sq, hp.N) *
+                                                         mla::kLkv * 4)
+                       : nullptr;
   a.qk_scale_log2 = scale * kv_scale * 1.4426950408889634f;
   a.out_scale = kv_scale;
   a.Sq = hp.Sq;
@@ -302,7 +304,9 @@ int mla_decode_reduce(mla_plan plan, void* o_latent, int64_t o_s_tok, int64_t o_
   m.reduce = plan->d_buf + plan->off_reduce;
   m.n_reduce = (int32_t)hp.reduce.size() / 3;
   m.ws_o = (float*)workspace;
-  m.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * R * mla::kLkv * 4) : nullptr;
+  m.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * mla::partial_rows(hp.Sq, hp.N) *
+                                                         mla::kLkv * 4)
+                       : nullptr;
   m.o = (uint16_t*)o_latent;
   m.o_s_tok = o_s_tok;
   m.o_s_head = o_s_head;

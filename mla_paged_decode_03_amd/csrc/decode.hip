@@ -660,15 +660,18 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
             }
           }
         } else {
-          float* prow = a.ws_o + ((int64_t)pidx * R + r) * kLkv;
+          // partial block of rows row0 + 32rb .. +31, in accumulator order: chunk q =
+          // 4 (32-column block) + gq holds 64 lanes x 4 floats (lane: row e32, columns
+          // 8 gq + 4 eh .. +3 of the block), so each store is 1 KB contiguous
+          float* pblk = a.ws_o + ((int64_t)pidx * partial_rows(a.Sq, a.N) + row0 + 32 * rb) * kLkv;
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             f32x16_t& acc = O[cb * NRB + rb];
             acc_fence(acc);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int col = 128 * w + 32 * cb + 8 * gq + 4 * eh;
-              *(f32x4_t*)(prow + col) =
+              const int q = 4 * (4 * w + cb) + gq;
+              *(f32x4_t*)(pblk + 4 * (64 * q + el)) =
                   f32x4_t{acc[4 * gq] * f, acc[4 * gq + 1] * f, acc[4 * gq + 2] * f, acc[4 * gq + 3] * f};
             }
           }
@@ -680,15 +683,41 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-// Software-pipelined variant for bf16 caches (one barrier per step).  Wave w owns query
-// rows 32w..32w+31 from end to end, with O (all 512 columns) in the 256 AGPRs and P in
-// VGPRs, so nothing but the key tile is shared.  Step s of a segment runs the 36 QK
-// MFMAs of tile q (with the DMA of a later tile between them), then the 32 P.V MFMAs
-// of tile q-1 with the softmax of tile q between them, so the MFMA pipe keeps working
-// through the VALU work.  A segment of n tiles takes n + 1 steps (no P.V in the
-// first, no QK in the last).  A stage is reloaded only after the P.V of the tile it
-// held, so up to two tiles are in flight beyond the two in use.
+// Software-pipelined kernel for bf16 caches.  Wave w owns query rows 32w..32w+31 from
+// end to end: Q in VGPRs, O (all 512 columns) in the 256 AGPRs and P in VGPRs, so only
+// the key tile is shared.  Step s of a segment of n tiles (s = 0..n):
+//   wait for tile s, barrier;
+//   QK of tile s (36 MFMAs), with this wave's DMA of a later tile between its MFMAs;
+//   P.V of tile s-1 (32 MFMAs), with the softmax of tile s between them;
+//   rescale of O when tile s raised a row's reference maximum (rare).
+// One loop body serves every step, so O stays in one set of registers: step 0 runs its
+// P.V with P = 0 against the landed tile 0, and step n a QK against tile n-1 whose
+// result is discarded (every key masked).  A stage is
+// reloaded once the P.V of the tile it held is complete, two steps before its QK.
+// With one wave per SIMD every instruction takes an issue slot of the MFMA stream, so
+// the per-tile address and bookkeeping work is kept small.
+//
+// Stage layout: key row k of the tile (576 bf16, latent then rope) at k * 1168 bytes,
+// a 16-byte pad after each row.  The odd 16-byte shift between rows (73 chunks) keeps
+// both read patterns free of bank conflicts (64 banks of 4 bytes; a 16-byte chunk's
+// bank group is its index mod 16) with addresses that are affine in the k-step:
+//  QK   ds_read_b128: S^T row i of the MFMA holds key pi(i) = ((i>>2)&3) + 4(i&3) +
+//       16(i>>4), a bijection that gives the 16 lanes of one access 16 keys with
+//       distinct residues mod 16, hence 16 distinct bank groups for the same chunk;
+//  P.V  ds_read_b64_tr_b16: with that order the 4 keys of one transposing read are
+//       {x, x+4, x+8, x+12}, 4 * 73 = 4 mod 16 bank groups apart, and each spans 4
+//       consecutive groups.
+// A tile is 2336 chunks, written by 37 DMA instructions of 1 KB (the last one half),
+// the pads receiving a copy of a neighbouring chunk.
 // ---------------------------------------------------------------------------------
+
+constexpr int kRowB = 1168;                  // LDS bytes per key row (576 bf16 + 16 pad)
+constexpr int kRowC = kRowB / 16;            // 73 chunks
+constexpr int kStageB = kTile * kRowB;       // 37376
+constexpr int kStageC = kTile * kRowC;       // 2336
+constexpr int kDmaN = (kStageC + 63) / 64;   // 37 DMA instructions per tile
+static_assert(kStages * kStageB <= kSmemBytes, "bf16 stages fit");
+static_assert(kDmaN == 37, "the last DMA instruction of a tile is the only partial one");
 
 // Calls f(std::integral_constant<int, K>) for K = 0..N-1 in order, as straight-line code.
 template <int N, typename F>
@@ -705,11 +734,40 @@ __device__ __forceinline__ void redef(T& x) { asm volatile("" : "+v"(x)); }
 template <typename T>
 __device__ __forceinline__ void use(const T& x) { asm volatile("" ::"v"(x)); }
 
-template <bool PAGED32>
-__global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
-  constexpr int PER = PAGED32 ? 9 : 16;  // DMA instructions per wave per tile
+// MFMAs whose A/B operands come from LDS or were written many instructions earlier
+// (no VALU write of them can sit right before): no leading wait states.
+__device__ __forceinline__ void mfma_v_first_nw(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_a_nw(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+
+// HBM -> LDS, 16 bytes per lane at lds_base + IMM + 16 lane, from gbase + voff.
+template <int IMM>
+__device__ __forceinline__ void dma16_si(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase),
+               "s"(lds_base), "n"(IMM)
+               : "memory", "m0", "scc");
+}
+
+// max(a, b, c) in one instruction (the inputs are finite or -inf: no NaN handling).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Tile key (0..31) held by S^T accumulator row i.
+__device__ __forceinline__ int row_key(int i) { return ((i >> 2) & 3) + 4 * (i & 3) + 16 * (i >> 4); }
+
+// FAST: pages of a multiple of 32 keys (a tile sits in one page) and the rope columns
+// right after the latent ones in each cache row (one base for the whole row).
+template <bool FAST>
+__global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
+  const int lane = tid & 63, r32 = lane & 31, h2 = lane >> 5;
 
   // Workgroups are dealt round-robin to the 8 XCDs; keep the head groups of
   // one part on one XCD so that they share its L2 for the part's keys.
@@ -725,29 +783,94 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   const int32_t* segs = a.segs;
   const int s_beg = ld_uniform(a.part_begin + part), s_end = ld_uniform(a.part_begin + part + 1);
   const float c = a.qk_scale_log2;
+  const uint32_t st = (uint32_t)a.s_tok * 2;  // bytes between cache rows
+  const uint32_t smem0 = lds_addr(smem);
+
+  // ---- DMA: wave w issues instructions j = w + 4n of a tile (n = 0..8, and n = 9 for
+  // wave 0: j = 36, lanes 0..31).  Lane l of instruction j writes stage chunk p = 64j + l
+  // = key p / 73, chunk p % 73 (the pad, chunk 72, takes a copy of chunk 71).
+  const bool w0 = w == 0;
+  auto chunk_key = [&](int n) __attribute__((always_inline)) { return (64 * (w + 4 * n) + lane) / kRowC; };
+  auto chunk_col = [&](int n) __attribute__((always_inline)) {
+    return min((64 * (w + 4 * n) + lane) % kRowC, kRowC - 2);
+  };
+  uint32_t dvo[10];  // FAST: byte offsets from the tile's first row
+#pragma unroll
+  for (int n = 0; n < 10; ++n) dvo[n] = (uint32_t)chunk_key(n) * st + 16u * (uint32_t)chunk_col(n);
+
+  auto dma_one = [&](const DmaTile& t, auto nc) __attribute__((always_inline)) {
+    constexpr int n = decltype(nc)::value;
+    if constexpr (n == 9) {
+      if (!w0 || lane >= 32) return;
+    }
+    if constexpr (FAST) {
+      dma16_si<4096 * n>(t.kv, dvo[n], t.lds + 1024 * w);
+    } else {
+      // generic pages: the rows of this instruction (at most two) through the block table
+      const int k0 = (64 * (w + 4 * n)) / kRowC;  // wave-uniform
+      const int64_t rb0 = row_bytes(a, t.bt_row, t.ts + min(k0, t.kmax), 2);
+      const int64_t rb1 = row_bytes(a, t.bt_row, t.ts + min(k0 + 1, t.kmax), 2);
+      const int col = chunk_col(n);
+      const int64_t rb = chunk_key(n) == k0 ? rb0 : rb1;
+      const char* src = col < 64 ? (const char*)t.kv + rb + 16 * col : (const char*)t.pe + rb + 16 * (col - 64);
+      dma16(src, t.lds + 1024 * (w + 4 * n));
+    }
+  };
+  // Keys past the segment end load key kmax instead (FAST: offsets moved to row kmax
+  // for the tile, dir = -1, and back, dir = +1).
+  auto dma_clamp = [&](const DmaTile& t, int dir) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < 10; ++n) dvo[n] += (uint32_t)(dir * max(chunk_key(n) - t.kmax, 0)) * st;
+  };
+  const int wkey = (64 * w + 64 * 4 * 9 + 63) / kRowC;  // upper bound of the keys this wave loads
+  auto dma_all = [&](const DmaTile& t) __attribute__((always_inline)) {
+    const bool clamp = FAST && t.kmax < wkey;
+    if (clamp) dma_clamp(t, -1);
+    static_for<10>([&](auto nc) __attribute__((always_inline)) { dma_one(t, nc); });
+    if (clamp) dma_clamp(t, 1);
+  };
+
+  // ---- LDS read addresses (bytes from a stage base) ----
+  // QK A operand: key row_key(r32), logical chunk 2k + h2 at kbase + 32 k.
+  const uint32_t kbase = (uint32_t)row_key(r32) * kRowB + 16 * h2;
+  // P.V A operand through ds_read_b64_tr_b16 (16-lane group g covers columns 32cb +
+  // 16(g & 1) + 0..15; lane j addresses key x + 4(j >> 2) at columns +4(j & 3) and
+  // receives those 4 keys of column +j): for k-step s the keys are x = h2 + 16s (e = 0..3)
+  // and x + 2 (e = 4..7), matching the B operand P^T = elements 8s..8s+7 of S^T.
+  const uint32_t vbase = (uint32_t)(h2 + 4 * ((lane & 15) >> 2)) * kRowB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   Cursor pf = first_tile(segs, s_beg, s_end);  // next tile to load
-  int issued = 0, tq = 0;                      // tiles issued; tiles whose QK has run
+  int issued = 0, done = 0;                    // tiles issued; tiles of finished segments
 #pragma unroll 1
-  for (int k = 0; k < kStages; ++k) issue_next<false, PAGED32>(a, segs, s_end, pf, issued, w);
+  for (int k = 0; k < kStages; ++k) {
+    if (pf.si >= s_end) break;
+    const DmaTile t = dma_tile<false, FAST>(a, pf, smem0 + (issued % kStages) * kStageB);
+    dma_all(t);
+    pf = next_tile(segs, pf, s_end);
+    issued++;
+  }
 
   for (int si = s_beg; si < s_end; ++si) {
     const Seg sg = load_seg(segs, si);
     const int b = sg.b, ks = sg.ks, ke = sg.ke, pidx = sg.pidx;
     const int L = ld_uniform(a.seq_lens + b);
+    const int nt = (ke - ks + kTile - 1) / kTile;
+    // keys j < lim are visible to this lane's row (segment end, causal window); every
+    // row sees at least the keys below lim_lo (wave-uniform)
+    const int lim_lo = min(ke, L - a.Sq + 1);
+    int lim = ke;
 
     // Query rows of this wave: B operand of S^T = K . Q^T, 36 x 8 bf16 per lane
     // (lane: row 32w + l%32, dims 16k + 8(l/32) .. +7 of k-step k).
     u32x4_t qr[36];
-    int lim = ke;  // keys j < lim are visible to this lane's row (segment end, causal window)
     if (has_rows) {
-      const int ql = lane_id(), rl = 32 * w + (ql & 31), qh = ql >> 5;
+      const int rl = 32 * w + r32;
       if (rl < RG) {
         const int r = row0 + rl;
         const int t = r / a.N, h = r - t * a.N;
         const int64_t tok = (int64_t)b * a.Sq + t;
-        const uint16_t* qn = a.q_nope + tok * a.q_nope_s_tok + (int64_t)h * a.q_nope_s_head + 8 * qh;
-        const uint16_t* qp = a.q_pe + tok * a.q_pe_s_tok + (int64_t)h * a.q_pe_s_head + 8 * qh;
+        const uint16_t* qn = a.q_nope + tok * a.q_nope_s_tok + (int64_t)h * a.q_nope_s_head + 8 * h2;
+        const uint16_t* qp = a.q_pe + tok * a.q_pe_s_tok + (int64_t)h * a.q_pe_s_head + 8 * h2;
 #pragma unroll
         for (int k = 0; k < 32; ++k) qr[k] = *(const u32x4_t*)(qn + 16 * k);
 #pragma unroll
@@ -769,75 +892,79 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
     float l_acc = 0.f;        // running sum over this lane's 16 keys of each tile
     f32x16_t O[16];           // O^T[32 cols of block cb][32 rows], in AGPRs
     acc_zero<16>(O);
-    uint32_t pkp[8];          // P of the previous tile: bf16 pairs, B operand of its P.V
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pkp[i] = 0;
+    f32x16_t sc;              // S^T of the tile in QK
+    // P of the previous tile as bf16 pairs: the B operands of its two P.V k-steps
+    u32x4_t pq[2] = {u32x4_t{0, 0, 0, 0}, u32x4_t{0, 0, 0, 0}};
 
-    const int nt = (ke - ks + kTile - 1) / kTile;
-    for (int st = 0; st < nt + (nt > 0 ? 1 : 0); ++st) {
-      const bool do_qk = st < nt, do_pv = st > 0;  // wave-uniform
-      if (do_qk) wait_tiles<PER>(issued - tq - 1);  // this wave's part of tile tq has landed
-      const int pv_done = tq - (do_pv ? 1 : 0);     // tiles whose P.V is complete
-      const bool do_dma = pf.si < s_end && issued < pv_done + kStages;
+    // (an empty request's segment has no tiles: no steps, and the epilogue writes o = 0,
+    // lse = -inf; the DMA cursor skips such segments)
+    const int g0 = done;  // part-wide index of the segment's first tile
+#pragma unroll 1
+    for (int s = 0; s <= nt && nt > 0; ++s) {
+      const int g = g0 + s;  // part-wide index of tile s (its stage is g % kStages)
+      const bool first = s == 0, last = s == nt;
+      // ---- wait for tile s, decide the DMA of this step, barrier ----
+      if (!last) {  // this wave's part of tile s has landed
+        if (w0) wait_tiles<10>(issued - g - 1);
+        else wait_tiles<9>(issued - g - 1);
+      }
+      // a stage is free once the P.V of its tile is complete: before this barrier, every
+      // tile up to g-2 (g-1 at the segment's first step)
+      const bool do_dma = pf.si < s_end && issued < g + (first ? kStages : kStages - 1);
       DmaTile dt{};
-      if (do_dma) dt = dma_tile<false, PAGED32>(a, pf, next_lds<false>(issued));
-      barrier_lds();  // tile tq has landed for every wave; the stage of tile tq-2 is free
-      const char* qst = smem + (tq % kStages) * kStageBytes;
-      const char* pst = smem + ((tq + kStages - 1) % kStages) * kStageBytes;
-      const int ts = ks + kTile * st;  // first key of tile tq
+      if (do_dma) dt = dma_tile<false, FAST>(a, pf, smem0 + ((unsigned)issued % kStages) * kStageB);
+      barrier_lds();  // tile s has landed for every wave; the stage of tile s-2 is free
+      const uint32_t qst = ((unsigned)(last ? g - 1 : g) % kStages) * kStageB;
+      const uint32_t pst = ((unsigned)(first ? g : g - 1) % kStages) * kStageB;
+      const int tq = ks + kTile * s;  // first key of tile s
 
       if (has_rows) {
-        const int ln = lane_id(), r32 = ln & 31, h2 = ln >> 5;
-        f32x16_t sc;
-        if (do_qk) {
-          // ---- S^T[32 keys][32 rows] = K . Q^T: 36 k-steps over the 576 dims ----
-          // A operand: key r32, logical chunk 2k + h2 = (2k) ^ h2, so its swizzled chunk
-          // is (2k) ^ (h2 ^ swz).  K fragments stream through a ring; one DMA step of a
-          // later tile follows every second MFMA from the fourth on.
-          const int kx = h2 ^ lat_swz(r32), rx = h2 ^ rope_swz(r32);
-          const char* kbase = qst + r32 * kLatRow;
-          const char* rbase = qst + kRopeOff + r32 * kRopeRow;
-          auto k_at = [&](int k) __attribute__((always_inline)) {
-            return k < 32 ? *(const u32x4_t*)(kbase + (((2 * (k & 7)) ^ kx) << 4) + 256 * (k >> 3))
-                          : *(const u32x4_t*)(rbase + (((2 * (k - 32)) ^ rx) << 4));
-          };
-          constexpr int KR = 6;  // K fragment ring depth
+        // the DMA goes between the QK MFMAs unless the tile ends inside this wave's rows
+        // (then it is issued here, with the clamped offsets)
+        const bool dma_il = do_dma && (!FAST || dt.kmax >= wkey);  // wave-uniform
+        if (do_dma && !dma_il) dma_all(dt);
+        // ---- S^T[32 keys][32 rows] = K . Q^T: 36 k-steps over the 576 dims, with this
+        // wave's DMA of a later tile between the MFMAs ----
+        {
+          const char* kp = smem + qst + kbase;
+          auto k_at = [&](int k) __attribute__((always_inline)) { return *(const u32x4_t*)(kp + 32 * k); };
+          constexpr int KR = 4;  // K fragment ring depth
           u32x4_t kb[KR];
 #pragma unroll
           for (int k = 0; k < KR; ++k) kb[k] = k_at(k);
           static_for<36>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             if constexpr (k == 0)
-              mfma_first(sc, kb[0], qr[0]);
+              mfma_v_first_nw(sc, kb[0], qr[0]);
             else if constexpr (k == 35)
               mfma_acc_v_last(sc, kb[k % KR], qr[k]);
             else
               mfma_acc_v(sc, kb[k % KR], qr[k]);
             if constexpr (k + KR < 36) kb[k % KR] = k_at(k + KR);
-            if constexpr (k >= 3 && (k - 3) % 2 == 0 && (k - 3) / 2 < kDmaSteps<false>) {
-              if (do_dma) dma_issue<false, PAGED32>(a, dt, (k - 3) / 2, w, lane_id());
+            if constexpr (k % 3 == 2 && k / 3 < 10) {
+              if (dma_il) dma_one(dt, std::integral_constant<int, k / 3>{});
             }
           });
-        } else if (do_dma) {
-#pragma unroll
-          for (int i = 0; i < kDmaSteps<false>; ++i) dma_issue<false, PAGED32>(a, dt, i, w, lane_id());
         }
 
-        // ---- softmax of tile tq in chunks (lane: row 32w + r32, keys ts + 8(v/4) + 4 h2
-        // + v%4), branch-free so that they stay between the P.V MFMAs ----
-        float mx = 0.f, fac = 1.f, nm = 0.f, psum = 0.f;
-        uint32_t pkn[8];
+        // ---- softmax of tile s in chunks (lane: row 32w + r32; element v holds key
+        // row_key(8(v/4) + 4 h2 + v%4) of the tile), each pinned between two P.V MFMAs;
+        // the last step's QK result is discarded (every key masked) ----
+        float mx = 0.f, fac = 1.f, nm = 0.f, pt[8], psum = 0.f;
         auto soft = [&](auto chc) __attribute__((always_inline)) {
           constexpr int ch = decltype(chc)::value;
           if constexpr (ch == 0) {
             redef(sc);
-            const int rem = lim - ts - 4 * h2;  // key offset 8(v/4) + v%4 is visible iff < rem
+            if (last || tq + kTile > lim_lo) {  // wave-uniform: some key of the tile is masked
+              const int rem = last ? 0 : lim - tq;  // tile key k is visible iff k < rem
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if (8 * (v >> 2) + (v & 3) >= rem) sc[v] = -INFINITY;
-            mx = sc[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+              for (int v = 0; v < 16; ++v)
+                if (row_key(8 * (v >> 2) + 4 * h2 + (v & 3)) >= rem) sc[v] = -INFINITY;
+            }
+            const float m0 = max3f(sc[0], sc[1], sc[2]), m1 = max3f(sc[3], sc[4], sc[5]);
+            const float m2 = max3f(sc[6], sc[7], sc[8]), m3 = max3f(sc[9], sc[10], sc[11]);
+            const float m4 = max3f(sc[12], sc[13], sc[14]);
+            mx = max3f(max3f(m0, m1, m2), max3f(m3, m4, sc[15]), -INFINITY);
             use(mx);
           } else if constexpr (ch == 1) {
             redef(mx);
@@ -852,107 +979,99 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             // exp2(-inf) = 0 covers masked keys; rows without a visible key keep m = -inf
             nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
             use(nm);
-          } else if constexpr (ch < 10) {
-            constexpr int v = 2 * (ch - 2);
+          } else if constexpr (ch < 6) {
+            // pair e of the first k-step, written in place once the old pair is dead
+            constexpr int e = ch - 2;
             redef(nm);
-            const float p0 = fast_exp2(fmaf(sc[v], c, nm));
-            const float p1 = fast_exp2(fmaf(sc[v + 1], c, nm));
+            const float p0 = fast_exp2(fmaf(sc[2 * e], c, nm));
+            const float p1 = fast_exp2(fmaf(sc[2 * e + 1], c, nm));
             psum += p0 + p1;
-            pkn[v >> 1] = pack_bf16x2(p0, p1);
-            use(pkn[v >> 1]);
+            pq[0][e] = pack_bf16x2(p0, p1);
+            use(pq[0][e]);
+            use(psum);
           } else {
-            l_acc += psum;
+            // pairs of the second k-step, kept in fp32 until the old ones are dead
+            constexpr int e = ch - 2;
+            redef(nm);
+            pt[2 * (e - 4)] = fast_exp2(fmaf(sc[2 * e], c, nm));
+            pt[2 * (e - 4) + 1] = fast_exp2(fmaf(sc[2 * e + 1], c, nm));
+            psum += pt[2 * (e - 4)] + pt[2 * (e - 4) + 1];
+            use(pt[2 * (e - 4)]);
+            use(pt[2 * (e - 4) + 1]);
+            use(psum);
           }
         };
 
-        if (do_pv) {
-          // ---- O^T[32 cols][32 rows] += V^T . P^T of tile tq-1, 16 keys per k-step ----
-          // B operand: P^T keys 16s + 4 h2 + (e & 3) + 8 (e >> 2), e = 0..7, which are
-          // elements 8s..8s+7 of this lane's S^T accumulator.  A operand: V^T through
-          // ds_read_b64_tr_b16: 16-lane group g covers columns 32cb + 16(g & 1) + 0..15
-          // and keys t0..t0+3 (t0 = 16s + 4(g >> 1), +8 for the second read); lane j
-          // addresses key t0 + j/4 at columns +4(j & 3) and receives keys t0..t0+3 of
-          // column +j.  Fragments stream through a 4-deep ring.
-          const int g = ln >> 4, j = ln & 15;
-          int vt_off[2][4];  // [key half][cb & 3]; + 256 (cb >> 2) + 16 KB s
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            const int key = 4 * h2 + (j >> 2) + 8 * kh;
-#pragma unroll
-            for (int cq = 0; cq < 4; ++cq) {
-              const int col = 32 * cq + 16 * (g & 1) + 4 * (j & 3);
-              vt_off[kh][cq] = key * kLatRow + (((col >> 3) ^ lat_swz(key)) << 4) + 8 * ((col >> 2) & 1);
-            }
-          }
-          auto vt_at = [&](int i) __attribute__((always_inline)) {  // fragment i = 16 s + cb
-            const int o = 256 * ((i & 15) >> 2) + 16 * kLatRow * (i >> 4);
-            return read_vt(pst + vt_off[0][i & 3] + o, pst + vt_off[1][i & 3] + o);
+        // ---- O^T[32 cols][32 rows] += V^T . P^T of tile s-1, 16 keys per k-step ----
+        // B operand: P^T = elements 8s'..8s'+7 of the previous tile's S^T (as bf16).
+        {
+          const char* vp = smem + pst + vbase;
+          auto vt_at = [&](int i) __attribute__((always_inline)) {  // fragment i = 16 s' + cb
+            const char* p = vp + (i >> 4) * 16 * kRowB + 64 * (i & 15);
+            return read_vt(p, p + 2 * kRowB);
           };
-          u32x4_t vb[4];
+          constexpr int VR = 3;
+          u32x4_t vb[VR];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vb[i] = vt_at(i);
+          for (int i = 0; i < VR; ++i) vb[i] = vt_at(i);
+          const u32x4_t p0 = pq[0], p1 = pq[1];
           static_for<32>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
             constexpr int sk = i >> 4, cb = i & 15;
-            const u32x4_t pf4 = u32x4_t{pkp[4 * sk], pkp[4 * sk + 1], pkp[4 * sk + 2], pkp[4 * sk + 3]};
-            if constexpr (i == 31)
-              mfma_acc_a_last(O[cb], vb[i & 3], pf4);
-            else
-              mfma_acc_a(O[cb], vb[i & 3], pf4);
-            if constexpr (i + 4 < 32) vb[i & 3] = vt_at(i + 4);
-            if constexpr (i >= 1 && i - 1 <= 10) {
-              if (do_qk) soft(std::integral_constant<int, i - 1>{});
-            }
+            mfma_a_nw(O[cb], vb[i % VR], sk ? p1 : p0);
+            if constexpr (i + VR < 32) vb[i % VR] = vt_at(i + VR);
+            // softmax chunks: the maximum and the reference early, the exponentials of a
+            // k-step's pairs after the last MFMA that reads that k-step's old pairs
+            if constexpr (i == 1) soft(std::integral_constant<int, 0>{});
+            if constexpr (i == 3) soft(std::integral_constant<int, 1>{});
+            if constexpr (i >= 16 && i % 2 == 0) soft(std::integral_constant<int, 2 + (i - 16) / 2>{});
           });
-        } else {
-          static_for<11>([&](auto chc) __attribute__((always_inline)) { soft(chc); });
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pq[1][e] = pack_bf16x2(pt[2 * e], pt[2 * e + 1]);
+        l_acc += psum;
 
-        if (do_qk) {
-          // rare: O rows whose reference maximum was raised by tile tq (O holds P.V up to
-          // tile tq-1, taken against the old reference)
-          if (__any(fac != 1.f)) {
+        // rare: O rows whose reference maximum was raised by tile s (O holds P.V up to
+        // tile s-1, taken against the old reference)
+        if (__any(fac != 1.f)) {
+          asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // the last P.V MFMA's result
 #pragma unroll
-            for (int cb = 0; cb < 16; ++cb) {
-              acc_fence(O[cb]);
+          for (int cb = 0; cb < 16; ++cb) {
+            acc_fence(O[cb]);
 #pragma unroll
-              for (int v = 0; v < 16; ++v) O[cb][v] *= fac;
-              acc_written(O[cb]);
-            }
+            for (int v = 0; v < 16; ++v) O[cb][v] *= fac;
+            acc_written(O[cb]);
           }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pkp[i] = pkn[i];
         }
       } else if (do_dma) {
-#pragma unroll
-        for (int i = 0; i < kDmaSteps<false>; ++i) dma_issue<false, PAGED32>(a, dt, i, w, lane_id());
+        dma_all(dt);
       }
       if (do_dma) {
         pf = next_tile(segs, pf, s_end);
         issued++;
       }
-      if (do_qk) tq++;
     }
+    done = g0 + nt;
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // the last P.V MFMA's result is read next
 
     // ---- epilogue: o = O * kv_scale / l, lse = ln(sum exp) ----
     if (has_rows) {
       const float l_row = half_sum(l_acc);
-      const int el = lane_id(), eh = el >> 5;
-      const int rl = 32 * w + (el & 31);
+      const int rl = 32 * w + r32;
       if (rl < RG) {
         const int r = row0 + rl;
         const float lse = (l_row > 0.f) ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
         const float f = (l_row > 0.f) ? a.out_scale / l_row : 0.f;
         const int t = r / a.N, h = r - t * a.N;
         if (pidx < 0) {
-          if (a.lse && eh == 0) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
+          if (a.lse && h2 == 0) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
           uint16_t* orow = a.o + ((int64_t)b * a.Sq + t) * a.o_s_tok + (int64_t)h * a.o_s_head;
 #pragma unroll
           for (int cb = 0; cb < 16; ++cb) {
             acc_fence(O[cb]);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int col = 32 * cb + 8 * gq + 4 * eh;
+              const int col = 32 * cb + 8 * gq + 4 * h2;
               u32x2_t pk2;
               pk2[0] = pack_bf16x2(O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f);
               pk2[1] = pack_bf16x2(O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f);
@@ -960,16 +1079,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             }
           }
         } else {
-          if (eh == 0) a.ws_lse[(int64_t)pidx * R + r] = lse;
-          float* prow = a.ws_o + ((int64_t)pidx * R + r) * kLkv;
+          if (h2 == 0) a.ws_lse[(int64_t)pidx * R + r] = lse;
+          // partial block of rows row0 + 32w .. +31 in accumulator order (chunk q = 4 cb +
+          // gq: 64 lanes x 4 floats), so each store is 1 KB contiguous
+          float* pblk = a.ws_o + ((int64_t)pidx * partial_rows(a.Sq, a.N) + row0 + 32 * w) * kLkv;
 #pragma unroll
           for (int cb = 0; cb < 16; ++cb) {
             acc_fence(O[cb]);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int col = 32 * cb + 8 * gq + 4 * eh;
-              *(f32x4_t*)(prow + col) = f32x4_t{O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f,
-                                                O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f};
+              *(f32x4_t*)(pblk + 4 * (64 * (4 * cb + gq) + lane)) =
+                  f32x4_t{O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f, O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f};
             }
           }
         }
@@ -1000,8 +1120,10 @@ hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
     if (p32) launch_nrb<true, true>(a, nrb, grid, stream);
     else launch_nrb<true, false>(a, nrb, grid, stream);
   } else {
-    if (p32) hipLaunchKernelGGL((mla_decode_pipe_kernel<true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_pipe_kernel<false>), grid, dim3(256), 0, stream, a);
+    // one base for the whole cache row: the rope columns follow the latent ones
+    const bool canon = (const char*)a.k_pe == (const char*)a.kv_c + 2 * kLkv;
+    if (p32 && canon) hipLaunchKernelGGL((mla_decode_bf16_kernel<true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_bf16_kernel<false>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

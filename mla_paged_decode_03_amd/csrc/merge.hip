@@ -4,7 +4,6 @@
 // docstring, "Chunked Prefill": merge_attn_states of prefix and suffix):
 //   m = max lse_i, w_i = exp(lse_i - m), o = sum w_i o_i / sum w_i,
 //   lse = m + ln sum w_i;  all -inf -> o = 0, lse = -inf.
-// One wave merges one row; each lane owns 8 consecutive columns per step.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,45 +11,66 @@ namespace mla {
 
 namespace {
 
+// Split-KV reduce: one workgroup per (request, block of 32 query rows, quarter of the
+// 512 columns).  The partial outputs of a row block are stored in the decode kernels'
+// accumulator order: chunk q = 4 (32-column block) + gq holds 64 lanes x 4 floats, lane l
+// covering row l % 32 and columns 8 gq + 4 (l / 32) .. +3 of that column block.  Wave w
+// of column quarter z merges the 4 chunks of column block 4z + w, one 1 KB load per chunk
+// and partial (the 4 in flight together); the result goes through LDS as a bf16
+// [32][128] tile and leaves as 256-byte row pieces.
+constexpr int kTileLd = 128 + 8;  // bf16 row stride of the output tile in LDS
 __global__ __launch_bounds__(256) void split_merge_kernel(MergeArgs a) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[32 * kTileLd];
   const int R = a.Sq * a.N;
-  const int red = blockIdx.x;
-  const int r = blockIdx.y * 4 + w;
-  if (red >= a.n_reduce || r >= R) return;
+  const int red = blockIdx.x, rb = blockIdx.y, zq = blockIdx.z;
+  if (red >= a.n_reduce || 32 * rb >= R) return;  // (whole workgroup)
   const int b = a.reduce[3 * red], base = a.reduce[3 * red + 1], n = a.reduce[3 * red + 2];
-  // Every lane derives the weights itself (n <= 64 broadcast loads): no LDS, no barrier.
-  const float* lse_i = a.ws_lse + (int64_t)base * R + r;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, rl = l & 31, h2 = l >> 5;
+  // this lane's row: reference m and 1 / sum of the weights (rows past R get none)
+  const int r = 32 * rb + rl;
+  const float* lse_i = a.ws_lse + (int64_t)base * R + min(r, R - 1);
   float m = -INFINITY;
-  for (int i = 0; i < n; ++i) m = fmaxf(m, lse_i[(int64_t)i * R]);
+  if (r < R)
+    for (int i = 0; i < n; ++i) m = fmaxf(m, lse_i[(int64_t)i * R]);
   const bool dead = (m == -INFINITY);
   float z = 0.f;
   if (!dead)
     for (int i = 0; i < n; ++i) z += fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e);
   const float inv = dead ? 0.f : 1.f / z;
-  const int col = 8 * l;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  if (!dead) {
-    for (int i = 0; i < n; ++i) {
-      const float wi = fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e) * inv;
-      const float* src = a.ws_o + ((int64_t)(base + i) * R + r) * kLkv + col;
-      const f32x4_t x0 = *(const f32x4_t*)src;
-      const f32x4_t x1 = *(const f32x4_t*)(src + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += wi * x0[e];
-        acc[4 + e] += wi * x1[e];
-      }
-    }
+  if (a.lse && zq == 0 && w == 0 && h2 == 0 && r < R) {
+    const int t = r / a.N, h = r - t * a.N;
+    a.lse[((int64_t)b * a.Sq + t) * a.N + h] = dead ? -INFINITY : m + fast_log2(z) * kLn2;
   }
-  const int t = r / a.N, h = r - t * a.N;
-  const int64_t tok = (int64_t)b * a.Sq + t;
-  uint16_t* dst = a.o + tok * a.o_s_tok + (int64_t)h * a.o_s_head + col;
-  *(u32x4_t*)dst = u32x4_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                           pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-  if (a.lse && l == 0) a.lse[tok * a.N + h] = dead ? -INFINITY : m + fast_log2(z) * kLn2;
+  const int64_t pstride = partial_rows(a.Sq, a.N) * kLkv;
+  const int cb = 4 * zq + w;  // column block of this wave
+  const float* src = a.ws_o + (int64_t)base * pstride + (int64_t)(32 * rb) * kLkv + 256 * (4 * cb) + 4 * l;
+  f32x4_t acc[4] = {};
+  for (int i = 0; i < n && !dead; ++i) {
+    const float wi = fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e) * inv;
+    f32x4_t x[4];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) x[gq] = *(const f32x4_t*)(src + (int64_t)i * pstride + 256 * gq);
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[gq][e] += wi * x[gq][e];
+  }
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    const int col = 32 * w + 8 * gq + 4 * h2;  // within this quarter
+    *(u32x2_t*)(tile + rl * kTileLd + col) =
+        u32x2_t{pack_bf16x2(acc[gq][0], acc[gq][1]), pack_bf16x2(acc[gq][2], acc[gq][3])};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + 256 * k, row = idx >> 4, c8 = idx & 15;
+    const int rr = 32 * rb + row;
+    if (rr >= R) continue;
+    const int t = rr / a.N, h = rr - t * a.N;
+    uint16_t* dst = a.o + ((int64_t)b * a.Sq + t) * a.o_s_tok + (int64_t)h * a.o_s_head + 128 * zq + 8 * c8;
+    *(u32x4_t*)dst = *(const u32x4_t*)(tile + row * kTileLd + 8 * c8);
+  }
 }
 
 __device__ __forceinline__ void load8(const void* p, bool fp32, float* x) {
@@ -124,7 +144,7 @@ __global__ void gather_rows_kernel(const int32_t* bt, int64_t bt_s, const int32_
 hipError_t launch_split_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.n_reduce == 0) return hipSuccess;
   const int R = a.Sq * a.N;
-  const dim3 grid(a.n_reduce, (R + 3) / 4), block(256);
+  const dim3 grid(a.n_reduce, (R + 31) / 32, 4), block(256);
   hipLaunchKernelGGL(split_merge_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }

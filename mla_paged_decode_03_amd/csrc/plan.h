@@ -27,6 +27,9 @@ struct Plan {
 };
 
 inline int32_t head_groups(int32_t Sq, int32_t N) { return (Sq * N + kGroupRows - 1) / kGroupRows; }
+// Rows of one partial output in the workspace: Sq*N rounded up to whole 32-row blocks
+// (a block is stored in the order of the MFMA accumulators, see the decode kernels).
+constexpr int64_t partial_rows(int32_t Sq, int32_t N) { return ((int64_t)Sq * N + 31) / 32 * 32; }
 
 // Builds the plan; returns false (with a message) only on invalid input.
 bool build_plan(const int32_t* seq_lens, int32_t B, int32_t Sq, int32_t N, int32_t num_cus,

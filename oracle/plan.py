@@ -101,8 +101,10 @@ def split_plan(seq_lens, Sq: int, N: int, num_cus: int):
 
 
 def workspace_bytes(num_partials: int, Sq: int, N: int, Lkv: int = 512) -> int:
-    """fp32 partial outputs [partials, Sq*N, Lkv] followed by fp32 partial LSE [partials, Sq*N]."""
-    return num_partials * Sq * N * (Lkv * 4 + 4)
+    """fp32 partial outputs [partials, Sq*N rounded up to whole 32-row blocks, Lkv] followed
+    by fp32 partial LSE [partials, Sq*N]."""
+    rows = (Sq * N + 31) // 32 * 32
+    return num_partials * (rows * Lkv * 4 + Sq * N * 4)
 
 
 def gather_rows_all(block_table, seq_lens, page_size: int):
