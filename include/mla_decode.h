@@ -104,8 +104,9 @@ int mla_plan_destroy(mla_plan plan);
  * (mla/common.py docstring, "Data-Movement Friendly Approach": SDPA of
  * [ql_nope | q_pe] against [kv_c | k_pe] with value kv_c; the page expansion
  * of rocm_aiter_mla, AiterMLAMetadataBuilder._build_decode.)  kv_scale is the
- * per-tensor dequantisation scale of an fp8 cache (1 for bf16).  A row with
- * n = 0 gets o_latent = 0 and lse = -inf.
+ * per-tensor dequantisation scale of an fp8 cache (1 for bf16).  scale and
+ * kv_scale must be finite and positive (MLA_ERR_INVALID_ARG otherwise).  A row
+ * with n = 0 gets o_latent = 0 and lse = -inf.
  *
  *  q_nope    [B*Sq, N, 512] bf16, absorbed query ql_nope; token stride q_nope_s_tok, head stride q_nope_s_head.
  *  q_pe      [B*Sq, N, 64] bf16, strides q_pe_s_tok, q_pe_s_head.

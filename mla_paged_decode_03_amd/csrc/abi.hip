@@ -125,7 +125,7 @@ int mla_decode_plan(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t
   p->seq_lens.assign(seq_lens_host, seq_lens_host + B);
   p->stream = (hipStream_t)stream;
   p->device = device;
-  p->ws_bytes = (size_t)p->host.num_partials * ((size_t)mla::partial_rows(Sq, N) * mla::kLkv * 4 + (size_t)Sq * N * 4);
+  p->ws_bytes = (size_t)p->host.num_partials * ((size_t)mla::partial_rows(Sq, N) * mla::kLkv * 4 + (size_t)Sq * N * 8);
 
   const size_t nseg = p->host.segs.size();
   p->off_part = 4 * nseg;
@@ -217,8 +217,8 @@ int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, i
       o_s_head < 1 || cache_s_page < 1 || cache_s_tok < 1 || block_table_s_req < plan->max_pages)
     return fail(MLA_ERR_INVALID_ARG, "bad stride");
   if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
-  if (!std::isfinite(scale) || !std::isfinite(kv_scale) || kv_scale <= 0.f)
-    return fail(MLA_ERR_INVALID_ARG, "scale and kv_scale must be finite, kv_scale > 0");
+  if (!std::isfinite(scale) || !std::isfinite(kv_scale) || scale <= 0.f || kv_scale <= 0.f)
+    return fail(MLA_ERR_INVALID_ARG, "scale and kv_scale must be finite and > 0");
   // 16-byte loads of the queries and of cache pieces (8 bf16 or 16 fp8 values), 8-byte
   // output stores; the kernel forms the byte offset of a key within a 32-key tile in 32 bits.
   const bool fp8 = plan->kv_dtype == MLA_DT_FP8_E4M3FN;
@@ -266,6 +266,7 @@ int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, i
   a.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * mla::partial_rows(hp.Sq, hp.N) *
                                                          mla::kLkv * 4)
                        : nullptr;
+  a.ws_l = workspace ? a.ws_lse + (size_t)hp.num_partials * R : nullptr;
   a.qk_scale_log2 = scale * kv_scale * 1.4426950408889634f;
   a.out_scale = kv_scale;
   a.Sq = hp.Sq;
@@ -307,6 +308,7 @@ int mla_decode_reduce(mla_plan plan, void* o_latent, int64_t o_s_tok, int64_t o_
   m.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * mla::partial_rows(hp.Sq, hp.N) *
                                                          mla::kLkv * 4)
                        : nullptr;
+  m.ws_l = workspace ? m.ws_lse + (size_t)hp.num_partials * R : nullptr;
   m.o = (uint16_t*)o_latent;
   m.o_s_tok = o_s_tok;
   m.o_s_head = o_s_head;

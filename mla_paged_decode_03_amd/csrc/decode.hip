@@ -630,6 +630,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
           if (a.lse) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
         } else {
           a.ws_lse[(int64_t)pidx * R + r] = lse;
+          a.ws_l[(int64_t)pidx * R + r] = l_row / a.out_scale;
         }
       }
     }
@@ -660,9 +661,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
             }
           }
         } else {
-          // partial block of rows row0 + 32rb .. +31, in accumulator order: chunk q =
-          // 4 (32-column block) + gq holds 64 lanes x 4 floats (lane: row e32, columns
-          // 8 gq + 4 eh .. +3 of the block), so each store is 1 KB contiguous
+          // unnormalised partial block of rows row0 + 32rb .. +31 (the reduce divides by
+          // the stored row sums), in accumulator order: chunk q = 4 (32-column block) + gq
+          // holds 64 lanes x 4 floats (lane: row e32, columns 8 gq + 4 eh .. +3 of the
+          // block), so each store is 1 KB contiguous, straight from the AGPRs
           float* pblk = a.ws_o + ((int64_t)pidx * partial_rows(a.Sq, a.N) + row0 + 32 * rb) * kLkv;
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
@@ -671,8 +673,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               const int q = 4 * (4 * w + cb) + gq;
-              *(f32x4_t*)(pblk + 4 * (64 * q + el)) =
-                  f32x4_t{acc[4 * gq] * f, acc[4 * gq + 1] * f, acc[4 * gq + 2] * f, acc[4 * gq + 3] * f};
+              *(f32x4_t*)(pblk + 4 * (64 * q + el)) = f32x4_t{acc[4 * gq], acc[4 * gq + 1], acc[4 * gq + 2], acc[4 * gq + 3]};
             }
           }
         }
@@ -751,11 +752,23 @@ __device__ __forceinline__ void dma16_si(const void* gbase, uint32_t voff, uint3
                : "memory", "m0", "scc");
 }
 
-// max(a, b, c) in one instruction (the inputs are finite or -inf: no NaN handling).
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+
+// Softmax ops as volatile statements, so that each stays in the slot between two MFMAs
+// where it is written (the compiler keeps volatile statements in order).  Their operands
+// come from ops at least one MFMA earlier, which also covers the one wait state a
+// transcendental result needs before its use.
+__device__ __forceinline__ void vmax3(float& d, float a, float b, float c) {
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+}
+__device__ __forceinline__ void vfma(float& d, float a, float b, float c) {
+  asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+}
+__device__ __forceinline__ void vexp2(float& d, float a) { asm volatile("v_exp_f32 %0, %1" : "=v"(d) : "v"(a)); }
+__device__ __forceinline__ void vadd(float& d, float a, float b) {
+  asm volatile("v_add_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void vcvt_bf16x2(uint32_t& d, float lo, float hi) {
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
 }
 
 // Tile key (0..31) held by S^T accumulator row i.
@@ -889,6 +902,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
     }
 
     float m_ref = -INFINITY;  // reference maximum of this lane's row (log2 units)
+    float nm = 0.f;           // exponent offset: -m_ref (0 while m_ref = -inf)
+    float thr = -INFINITY;    // (m_ref + 8) / c: elements of S above it need a new reference
     float l_acc = 0.f;        // running sum over this lane's 16 keys of each tile
     f32x16_t O[16];           // O^T[32 cols of block cb][32 rows], in AGPRs
     acc_zero<16>(O);
@@ -918,14 +933,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
       const uint32_t pst = ((unsigned)(first ? g : g - 1) % kStages) * kStageB;
       const int tq = ks + kTile * s;  // first key of tile s
 
+      if (has_rows && last && do_dma) dma_all(dt);  // the segment's last step has no QK
       if (has_rows) {
         // the DMA goes between the QK MFMAs unless the tile ends inside this wave's rows
         // (then it is issued here, with the clamped offsets)
         const bool dma_il = do_dma && (!FAST || dt.kmax >= wkey);  // wave-uniform
-        if (do_dma && !dma_il) dma_all(dt);
+        if (!last && do_dma && !dma_il) dma_all(dt);
         // ---- S^T[32 keys][32 rows] = K . Q^T: 36 k-steps over the 576 dims, with this
         // wave's DMA of a later tile between the MFMAs ----
-        {
+        if (!last) {
           const char* kp = smem + qst + kbase;
           auto k_at = [&](int k) __attribute__((always_inline)) { return *(const u32x4_t*)(kp + 32 * k); };
           constexpr int KR = 4;  // K fragment ring depth
@@ -947,59 +963,58 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
           });
         }
 
-        // ---- softmax of tile s in chunks (lane: row 32w + r32; element v holds key
-        // row_key(8(v/4) + 4 h2 + v%4) of the tile), each pinned between two P.V MFMAs;
-        // the last step's QK result is discarded (every key masked) ----
-        float mx = 0.f, fac = 1.f, nm = 0.f, pt[8], psum = 0.f;
-        auto soft = [&](auto chc) __attribute__((always_inline)) {
-          constexpr int ch = decltype(chc)::value;
-          if constexpr (ch == 0) {
-            redef(sc);
-            if (last || tq + kTile > lim_lo) {  // wave-uniform: some key of the tile is masked
-              const int rem = last ? 0 : lim - tq;  // tile key k is visible iff k < rem
+        // ---- softmax of tile s, spread over the P.V chain below (lane: row 32w + r32;
+        // element v holds key row_key(8(v/4) + 4 h2 + v%4) of the tile).  The
+        // exponentials are taken against the current reference (exponent offset nm); it
+        // stands unless a key exceeds it by more than 2^8, which this lane can test on its
+        // own maximum against thr (the reference plus 8, in units of S).  When some lane
+        // fails the test (a segment's first visible keys, then rarely) the tile is redone
+        // after the chain.  Every op is a volatile statement in a fixed slot after an
+        // MFMA, at least one slot after the ops it reads. ----
+        if (last || tq + kTile > lim_lo) {  // wave-uniform: some key of the tile is masked
+          const int rem = last ? 0 : lim - tq;  // tile key k is visible iff k < rem
 #pragma unroll
-              for (int v = 0; v < 16; ++v)
-                if (row_key(8 * (v >> 2) + 4 * h2 + (v & 3)) >= rem) sc[v] = -INFINITY;
-            }
-            const float m0 = max3f(sc[0], sc[1], sc[2]), m1 = max3f(sc[3], sc[4], sc[5]);
-            const float m2 = max3f(sc[6], sc[7], sc[8]), m3 = max3f(sc[9], sc[10], sc[11]);
-            const float m4 = max3f(sc[12], sc[13], sc[14]);
-            mx = max3f(max3f(m0, m1, m2), max3f(m3, m4, sc[15]), -INFINITY);
-            use(mx);
-          } else if constexpr (ch == 1) {
-            redef(mx);
-            mx = half_max(mx) * c;
-            // raise the reference when a tile exceeds it by more than 2^8 (the first tile
-            // with visible keys raises it from -inf, with nothing to rescale yet)
-            const bool need = __any(mx > m_ref + kRescaleAt);
-            const float m_new = need ? fmaxf(m_ref, mx) : m_ref;
-            fac = (m_new > m_ref && m_ref != -INFINITY) ? fast_exp2(m_ref - m_new) : 1.f;
-            l_acc *= fac;
-            m_ref = m_new;
-            // exp2(-inf) = 0 covers masked keys; rows without a visible key keep m = -inf
-            nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
-            use(nm);
-          } else if constexpr (ch < 6) {
-            // pair e of the first k-step, written in place once the old pair is dead
-            constexpr int e = ch - 2;
-            redef(nm);
-            const float p0 = fast_exp2(fmaf(sc[2 * e], c, nm));
-            const float p1 = fast_exp2(fmaf(sc[2 * e + 1], c, nm));
-            psum += p0 + p1;
-            pq[0][e] = pack_bf16x2(p0, p1);
-            use(pq[0][e]);
-            use(psum);
-          } else {
-            // pairs of the second k-step, kept in fp32 until the old ones are dead
-            constexpr int e = ch - 2;
-            redef(nm);
-            pt[2 * (e - 4)] = fast_exp2(fmaf(sc[2 * e], c, nm));
-            pt[2 * (e - 4) + 1] = fast_exp2(fmaf(sc[2 * e + 1], c, nm));
-            psum += pt[2 * (e - 4)] + pt[2 * (e - 4) + 1];
-            use(pt[2 * (e - 4)]);
-            use(pt[2 * (e - 4) + 1]);
-            use(psum);
+          for (int v = 0; v < 16; ++v)
+            if (row_key(8 * (v >> 2) + 4 * h2 + (v & 3)) >= rem) sc[v] = -INFINITY;
+        }
+        float mt[5], mf, mg, mx, ar[16], ex[16], tp[8], psum = 0.f;
+        auto slot = [&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value;
+          // this lane's maximum: a tree of v_max3 over slots 0..3
+          if constexpr (i == 0) {
+            vmax3(mt[0], sc[0], sc[1], sc[2]);
+            vmax3(mt[1], sc[3], sc[4], sc[5]);
+            vmax3(mt[2], sc[6], sc[7], sc[8]);
           }
+          if constexpr (i == 1) {
+            vmax3(mt[3], sc[9], sc[10], sc[11]);
+            vmax3(mt[4], sc[12], sc[13], sc[14]);
+            vmax3(mf, mt[0], mt[1], mt[2]);
+          }
+          if constexpr (i == 2) vmax3(mg, mt[3], mt[4], sc[15]);
+          if constexpr (i == 3) vmax3(mx, mf, mg, mg);
+          // pair k = elements 2k, 2k+1: fma at slot F, exp at F+1, pair sum at F+2, row sum
+          // at F+3; pairs 4..7 first (kept in fp32 until their old P.V operand is dead),
+          // then pairs 0..3, packed in place once the first k-step's MFMAs are issued
+          static_for<8>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            constexpr int F = k >= 4 ? 2 + 2 * (k - 4) : 14 + 2 * k;
+            if constexpr (i == F) {
+              vfma(ar[2 * k], sc[2 * k], c, nm);
+              vfma(ar[2 * k + 1], sc[2 * k + 1], c, nm);
+            }
+            if constexpr (i == F + 1) {
+              vexp2(ex[2 * k], ar[2 * k]);
+              vexp2(ex[2 * k + 1], ar[2 * k + 1]);
+            }
+            if constexpr (i == F + 2) vadd(tp[k], ex[2 * k], ex[2 * k + 1]);
+            if constexpr (i == F + 3) vadd(psum, psum, tp[k]);
+            if constexpr (k < 4 && i == F + 3) {
+              uint32_t pk;
+              vcvt_bf16x2(pk, ex[2 * k], ex[2 * k + 1]);
+              pq[0][k] = pk;
+            }
+          });
         };
 
         // ---- O^T[32 cols][32 rows] += V^T . P^T of tile s-1, 16 keys per k-step ----
@@ -1020,19 +1035,34 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
             constexpr int sk = i >> 4, cb = i & 15;
             mfma_a_nw(O[cb], vb[i % VR], sk ? p1 : p0);
             if constexpr (i + VR < 32) vb[i % VR] = vt_at(i + VR);
-            // softmax chunks: the maximum and the reference early, the exponentials of a
-            // k-step's pairs after the last MFMA that reads that k-step's old pairs
-            if constexpr (i == 1) soft(std::integral_constant<int, 0>{});
-            if constexpr (i == 3) soft(std::integral_constant<int, 1>{});
-            if constexpr (i >= 16 && i % 2 == 0) soft(std::integral_constant<int, 2 + (i - 16) / 2>{});
+            slot(ic);
           });
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pq[1][e] = pack_bf16x2(pt[2 * e], pt[2 * e + 1]);
-        l_acc += psum;
 
-        // rare: O rows whose reference maximum was raised by tile s (O holds P.V up to
-        // tile s-1, taken against the old reference)
+        float fac = 1.f;
+        if (__any(mx > thr)) {
+          // redo the tile against a raised reference: the row maximum (both halves), the
+          // factor for O and l (1 for the segment's first visible keys), new exponentials
+          const float mr = half_max(mx) * c;
+          const float m_new = fmaxf(m_ref, mr);
+          fac = (m_new > m_ref && m_ref != -INFINITY) ? fast_exp2(m_ref - m_new) : 1.f;
+          m_ref = m_new;
+          nm = (m_ref == -INFINITY) ? 0.f : -m_ref;  // exp2(-inf) = 0 covers masked keys
+          thr = (m_ref == -INFINITY) ? -INFINITY : (m_ref + kRescaleAt) / c;
+          float ps = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float e0 = fast_exp2(fmaf(sc[2 * k], c, nm)), e1 = fast_exp2(fmaf(sc[2 * k + 1], c, nm));
+            ps += e0 + e1;
+            pq[k >> 2][k & 3] = pack_bf16x2(e0, e1);
+          }
+          l_acc = l_acc * fac + ps;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pq[1][k] = pack_bf16x2(ex[8 + 2 * k], ex[9 + 2 * k]);
+          l_acc += psum;
+        }
+        // rare: O holds P.V up to tile s-1, taken against the old reference
         if (__any(fac != 1.f)) {
           asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // the last P.V MFMA's result
 #pragma unroll
@@ -1079,18 +1109,21 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
             }
           }
         } else {
-          if (h2 == 0) a.ws_lse[(int64_t)pidx * R + r] = lse;
-          // partial block of rows row0 + 32w .. +31 in accumulator order (chunk q = 4 cb +
-          // gq: 64 lanes x 4 floats), so each store is 1 KB contiguous
+          if (h2 == 0) {
+            a.ws_lse[(int64_t)pidx * R + r] = lse;
+            a.ws_l[(int64_t)pidx * R + r] = l_row / a.out_scale;
+          }
+          // unnormalised partial block of rows row0 + 32w .. +31 (the reduce divides by the
+          // stored row sums) in accumulator order (chunk q = 4 cb + gq: 64 lanes x 4
+          // floats), so each store is 1 KB contiguous, straight from the AGPRs
           float* pblk = a.ws_o + ((int64_t)pidx * partial_rows(a.Sq, a.N) + row0 + 32 * w) * kLkv;
 #pragma unroll
           for (int cb = 0; cb < 16; ++cb) {
             acc_fence(O[cb]);
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
+            for (int gq = 0; gq < 4; ++gq)
               *(f32x4_t*)(pblk + 4 * (64 * (4 * cb + gq) + lane)) =
-                  f32x4_t{O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f, O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f};
-            }
+                  f32x4_t{O[cb][4 * gq], O[cb][4 * gq + 1], O[cb][4 * gq + 2], O[cb][4 * gq + 3]};
           }
         }
       }

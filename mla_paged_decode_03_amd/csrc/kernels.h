@@ -25,6 +25,7 @@ struct DecodeArgs {
   float* lse;                 // [T, N] or null
   float* ws_o;                // [partials, Sq*N, 512]
   float* ws_lse;              // [partials, Sq*N]
+  float* ws_l;                // [partials, Sq*N]: row sums / kv_scale
   float qk_scale_log2;        // scale * kv_scale * log2(e)
   float out_scale;            // kv_scale
   int32_t Sq, N, page_size, num_parts, head_groups;
@@ -35,6 +36,7 @@ struct MergeArgs {
   int32_t n_reduce;
   const float* ws_o;
   const float* ws_lse;
+  const float* ws_l;
   uint16_t* o;
   int64_t o_s_tok, o_s_head;
   float* lse;

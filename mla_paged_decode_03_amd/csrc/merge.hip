@@ -12,8 +12,10 @@ namespace mla {
 namespace {
 
 // Split-KV reduce: one workgroup per (request, block of 32 query rows, quarter of the
-// 512 columns).  The partial outputs of a row block are stored in the decode kernels'
-// accumulator order: chunk q = 4 (32-column block) + gq holds 64 lanes x 4 floats, lane l
+// 512 columns).  Partial i of a row holds its unnormalised output O_i = sum_j p_j v_j, its
+// row sum l_i / kv_scale and its lse_i, so o = sum_i exp(lse_i - m) O_i / l_i / z with
+// z = sum_i exp(lse_i - m) (the merge above).  The partial outputs of a row block are
+// stored in the decode kernels' accumulator order: chunk q = 4 (32-column block) + gq holds 64 lanes x 4 floats, lane l
 // covering row l % 32 and columns 8 gq + 4 (l / 32) .. +3 of that column block.  Wave w
 // of column quarter z merges the 4 chunks of column block 4z + w, one 1 KB load per chunk
 // and partial (the 4 in flight together); the result goes through LDS as a bf16
@@ -29,6 +31,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeArgs a) {
   // this lane's row: reference m and 1 / sum of the weights (rows past R get none)
   const int r = 32 * rb + rl;
   const float* lse_i = a.ws_lse + (int64_t)base * R + min(r, R - 1);
+  const float* l_i = a.ws_l + (int64_t)base * R + min(r, R - 1);
   float m = -INFINITY;
   if (r < R)
     for (int i = 0; i < n; ++i) m = fmaxf(m, lse_i[(int64_t)i * R]);
@@ -46,7 +49,11 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeArgs a) {
   const float* src = a.ws_o + (int64_t)base * pstride + (int64_t)(32 * rb) * kLkv + 256 * (4 * cb) + 4 * l;
   f32x4_t acc[4] = {};
   for (int i = 0; i < n && !dead; ++i) {
-    const float wi = fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e) * inv;
+    // the partials are unnormalised: weight exp(lse_i - m) / z over the stored row sum
+    // (row sum / kv_scale, so the value scale comes in too); rows of a partial that saw
+    // no key have lse -inf, weight 0
+    const float li = l_i[(int64_t)i * R];
+    const float wi = li > 0.f ? fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e) * inv / li : 0.f;
     f32x4_t x[4];
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) x[gq] = *(const f32x4_t*)(src + (int64_t)i * pstride + 256 * gq);

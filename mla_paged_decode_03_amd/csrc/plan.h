@@ -10,7 +10,7 @@ constexpr int kLkv = 512;
 constexpr int kRope = 64;
 constexpr int kHead = kLkv + kRope;
 constexpr int kGranule = 64;    // keys per planning granule
-constexpr int kSegCost = 1;     // cost of a segment (query load + epilogue), in granules
+constexpr int kSegCost = 3;     // cost of a segment (query load + epilogue), in granules
 constexpr int kMinChunk = 4;    // smallest chunk taken to top up a part that already has work
 constexpr int kGroupRows = 128;  // query rows per head group (one workgroup)
 

@@ -9,7 +9,7 @@ key range covered exactly once, in order; partial slots contiguous; part count
 within the CU budget), not by the pages.
 
 Rule (integers only):
-  g = 64 keys per granule; c0 = 1 granule of cost per segment; MINC = 4.
+  g = 64 keys per granule; c0 = 3 granules of cost per segment; MINC = 4.
   rows per request R = Sq*N; head groups HG = ceil(R / 128).
   part budget P = max(1, floor(C / HG)) for C compute units.
   G_b = ceil(L_b / g); W = sum_b (G_b + c0).
@@ -28,7 +28,7 @@ Rule (integers only):
 from __future__ import annotations
 
 GRANULE = 64
-SEG_COST = 1
+SEG_COST = 3
 MIN_CHUNK = 4
 GROUP_ROWS = 128
 
@@ -101,10 +101,10 @@ def split_plan(seq_lens, Sq: int, N: int, num_cus: int):
 
 
 def workspace_bytes(num_partials: int, Sq: int, N: int, Lkv: int = 512) -> int:
-    """fp32 partial outputs [partials, Sq*N rounded up to whole 32-row blocks, Lkv] followed
-    by fp32 partial LSE [partials, Sq*N]."""
+    """fp32 partial outputs [partials, Sq*N rounded up to whole 32-row blocks, Lkv], then
+    fp32 partial LSE [partials, Sq*N] and fp32 partial row sums [partials, Sq*N]."""
     rows = (Sq * N + 31) // 32 * 32
-    return num_partials * (rows * Lkv * 4 + Sq * N * 4)
+    return num_partials * (rows * Lkv * 4 + Sq * N * 8)
 
 
 def gather_rows_all(block_table, seq_lens, page_size: int):
