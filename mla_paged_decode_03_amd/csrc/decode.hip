@@ -774,10 +774,20 @@ __device__ __forceinline__ void vcvt_bf16x2(uint32_t& d, float lo, float hi) {
 // Tile key (0..31) held by S^T accumulator row i.
 __device__ __forceinline__ int row_key(int i) { return ((i >> 2) & 3) + 4 * (i & 3) + 16 * (i >> 4); }
 
+// fp8 caches: 3 bf16 stages, then a ring of raw e4m3 tiles: wave w owns two slots of
+// 8 rows x 576 bytes (the rows it loads and widens).
+constexpr int kRawWaveTile = 8 * kHead;       // 4608
+constexpr int kRawBase = 3 * kStageB;         // 112128
+static_assert(kRawBase + 4 * 2 * kRawWaveTile <= kSmemBytes, "fp8 stages fit");
+
 // FAST: pages of a multiple of 32 keys (a tile sits in one page) and the rope columns
 // right after the latent ones in each cache row (one base for the whole row).
-template <bool FAST>
-__global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
+// FP8: e4m3 cache, widened to bf16 in LDS (every e4m3 value is exact in bf16).
+template <bool FAST, bool FP8>
+__global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
+  // K fragment ring depth, and DMA steps issued before the first QK MFMA (they fill the
+  // wait for the first fragments); chosen by measurement on the DSV3 and verify shapes
+  constexpr int KRING = 6, DMA0 = 2;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
   const int lane = tid & 63, r32 = lane & 31, h2 = lane >> 5;
@@ -796,8 +806,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
   const int32_t* segs = a.segs;
   const int s_beg = ld_uniform(a.part_begin + part), s_end = ld_uniform(a.part_begin + part + 1);
   const float c = a.qk_scale_log2;
-  const uint32_t st = (uint32_t)a.s_tok * 2;  // bytes between cache rows
+  const uint32_t st = (uint32_t)a.s_tok * (FP8 ? 1 : 2);  // bytes between cache rows
   const uint32_t smem0 = lds_addr(smem);
+  constexpr int NST = FP8 ? 3 : kStages;  // bf16 stages
 
   // ---- DMA: wave w issues instructions j = w + 4n of a tile (n = 0..8, and n = 9 for
   // wave 0: j = 36, lanes 0..31).  Lane l of instruction j writes stage chunk p = 64j + l
@@ -843,6 +854,55 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
     if (clamp) dma_clamp(t, 1);
   };
 
+  // ---- fp8: wave w loads rows 8w..8w+7 of a tile as raw e4m3 into its own slot of a
+  // two-tile ring and widens them into the bf16 stage one step before the QK that reads
+  // them; no other wave reads the slot, so it is refilled without a barrier.  DMA
+  // instruction n = 0..4 (4: lanes 0..31) covers raw chunk p = 64n + lane of the wave's
+  // rows: row p / 36, 16-byte chunk p % 36.
+  auto raw_row = [&](int n) __attribute__((always_inline)) { return (64 * n + lane) / 36; };
+  auto raw_col = [&](int n) __attribute__((always_inline)) { return (64 * n + lane) % 36; };
+  uint32_t rvo[5];  // FAST: byte offsets from the tile's first row
+#pragma unroll
+  for (int n = 0; n < 5; ++n) rvo[n] = (uint32_t)(8 * w + raw_row(n)) * st + 16u * (uint32_t)raw_col(n);
+  auto raw_slot = [&](int gi) __attribute__((always_inline)) {
+    return smem0 + kRawBase + (uint32_t)(2 * w + (gi & 1)) * kRawWaveTile;
+  };
+  auto dma_raw = [&](const DmaTile& t) __attribute__((always_inline)) {
+    const bool clamp = t.kmax < 8 * w + 7;  // wave-uniform: the tile ends inside these rows
+    static_for<5>([&](auto nc) __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value;
+      if constexpr (n == 4) {
+        if (lane >= 32) return;
+      }
+      if constexpr (FAST) {
+        uint32_t off = rvo[n];
+        if (clamp) off -= (uint32_t)max(8 * w + raw_row(n) - t.kmax, 0) * st;
+        dma16_si<1024 * n>(t.kv, off, t.lds);
+      } else {
+        // generic pages: the rows of this instruction (at most three) through the block table
+        const int k0 = 8 * w + (64 * n) / 36;  // wave-uniform
+        const int64_t rb0 = row_bytes(a, t.bt_row, t.ts + min(k0, t.kmax), 1);
+        const int64_t rb1 = row_bytes(a, t.bt_row, t.ts + min(k0 + 1, t.kmax), 1);
+        const int64_t rb2 = row_bytes(a, t.bt_row, t.ts + min(k0 + 2, t.kmax), 1);
+        const int kr = 8 * w + raw_row(n) - k0, col = raw_col(n);
+        const int64_t rb = kr == 0 ? rb0 : (kr == 1 ? rb1 : rb2);
+        const char* src = col < 32 ? (const char*)t.kv + rb + 16 * col : (const char*)t.pe + rb + 16 * (col - 32);
+        dma16(src, t.lds + 1024 * n);
+      }
+    });
+  };
+  // Widens chunk i of this wave's raw rows (slot `raw`, LDS address) into the bf16 stage
+  // at byte offset `dst` of smem: i < 8 is row i, values 8 lane .. +7 (latent); i = 8 is
+  // row lane / 8, rope values 8 (lane % 8) .. +7.
+  auto widen = [&](uint32_t raw, uint32_t dst, auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    const int row = i < 8 ? i : (lane >> 3);
+    const int col8 = i < 8 ? lane : 64 + (lane & 7);
+    const u32x2_t v = *(const u32x2_t*)(smem + (raw - smem0) + row * kHead + 8 * col8);
+    const u32x2_t lo = fp8x4_to_bf16x4(v[0]), hi = fp8x4_to_bf16x4(v[1]);
+    *(u32x4_t*)(smem + dst + (8 * w + row) * kRowB + 16 * col8) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  };
+
   // ---- LDS read addresses (bytes from a stage base) ----
   // QK A operand: key row_key(r32), logical chunk 2k + h2 at kbase + 32 k.
   const uint32_t kbase = (uint32_t)row_key(r32) * kRowB + 16 * h2;
@@ -854,13 +914,36 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
 
   Cursor pf = first_tile(segs, s_beg, s_end);  // next tile to load
   int issued = 0, done = 0;                    // tiles issued; tiles of finished segments
+  int widened = 0;                             // fp8: tiles widened into their bf16 stage
+  if constexpr (FP8) {
+    // raw tiles 0 and 1, tile 0 widened into stage 0, raw tile 2 into the freed slot
 #pragma unroll 1
-  for (int k = 0; k < kStages; ++k) {
-    if (pf.si >= s_end) break;
-    const DmaTile t = dma_tile<false, FAST>(a, pf, smem0 + (issued % kStages) * kStageB);
-    dma_all(t);
-    pf = next_tile(segs, pf, s_end);
-    issued++;
+    for (int k = 0; k < 2; ++k) {
+      if (pf.si >= s_end) break;
+      dma_raw(dma_tile<true, FAST>(a, pf, raw_slot(issued)));
+      pf = next_tile(segs, pf, s_end);
+      issued++;
+    }
+    if (issued > 0) {
+      if (issued > 1) wait_vm<5>();
+      else wait_vm<0>();
+      static_for<9>([&](auto ic) __attribute__((always_inline)) { widen(raw_slot(0), 0, ic); });
+      widened = 1;
+      if (pf.si < s_end) {
+        dma_raw(dma_tile<true, FAST>(a, pf, raw_slot(issued)));
+        pf = next_tile(segs, pf, s_end);
+        issued++;
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int k = 0; k < kStages; ++k) {
+      if (pf.si >= s_end) break;
+      const DmaTile t = dma_tile<false, FAST>(a, pf, smem0 + (issued % kStages) * kStageB);
+      dma_all(t);
+      pf = next_tile(segs, pf, s_end);
+      issued++;
+    }
   }
 
   for (int si = s_beg; si < s_end; ++si) {
@@ -919,35 +1002,66 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
       const int g = g0 + s;  // part-wide index of tile s (its stage is g % kStages)
       const bool first = s == 0, last = s == nt;
       // ---- wait for tile s, decide the DMA of this step, barrier ----
-      if (!last) {  // this wave's part of tile s has landed
-        if (w0) wait_tiles<10>(issued - g - 1);
-        else wait_tiles<9>(issued - g - 1);
-      }
-      // a stage is free once the P.V of its tile is complete: before this barrier, every
-      // tile up to g-2 (g-1 at the segment's first step)
-      const bool do_dma = pf.si < s_end && issued < g + (first ? kStages : kStages - 1);
+      bool do_dma;
       DmaTile dt{};
-      if (do_dma) dt = dma_tile<false, FAST>(a, pf, smem0 + ((unsigned)issued % kStages) * kStageB);
-      barrier_lds();  // tile s has landed for every wave; the stage of tile s-2 is free
-      const uint32_t qst = ((unsigned)(last ? g - 1 : g) % kStages) * kStageB;
-      const uint32_t pst = ((unsigned)(first ? g : g - 1) % kStages) * kStageB;
+      // fp8: tile s was widened before; this step widens tile s+1 (once: the last step of
+      // a segment and the first of the next have the same s) into the stage of tile s-2,
+      // then loads the next raw tile into the slot that frees
+      const bool widen_next = FP8 && widened == g + 1 && widened < issued;  // wave-uniform
+      if constexpr (FP8) {
+        do_dma = pf.si < s_end && issued < widened + (widen_next ? 3 : 2);
+        if (do_dma) dt = dma_tile<true, FAST>(a, pf, raw_slot(issued));
+      } else {
+        if (!last) {  // this wave's part of tile s has landed
+          if (w0) wait_tiles<10>(issued - g - 1);
+          else wait_tiles<9>(issued - g - 1);
+        }
+        // a stage is free once the P.V of its tile is complete: before this barrier, every
+        // tile up to g-2 (g-1 at the segment's first step)
+        do_dma = pf.si < s_end && issued < g + (first ? kStages : kStages - 1);
+        if (do_dma) dt = dma_tile<false, FAST>(a, pf, smem0 + ((unsigned)issued % kStages) * kStageB);
+      }
+      barrier_lds();  // tile s is in its stage for every wave; the stage of tile s-2 is free
+      const uint32_t qst = ((unsigned)(last ? g - 1 : g) % NST) * kStageB;
+      const uint32_t pst = ((unsigned)(first ? g : g - 1) % NST) * kStageB;
+      const uint32_t wst = ((unsigned)(g + 1) % NST) * kStageB;
+      auto raw_ready = [&]() __attribute__((always_inline)) {
+        if (issued > g + 2) wait_vm<5>();  // raw tile s+2 may still be in flight
+        else wait_vm<0>();
+      };
       const int tq = ks + kTile * s;  // first key of tile s
 
-      if (has_rows && last && do_dma) dma_all(dt);  // the segment's last step has no QK
+      if (has_rows && last) {  // the segment's last step has no QK
+        if constexpr (FP8) {
+          if (widen_next) {
+            raw_ready();
+            static_for<9>([&](auto ic) __attribute__((always_inline)) { widen(raw_slot(g + 1), wst, ic); });
+          }
+          if (do_dma) dma_raw(dt);
+        } else {
+          if (do_dma) dma_all(dt);
+        }
+      }
       if (has_rows) {
         // the DMA goes between the QK MFMAs unless the tile ends inside this wave's rows
         // (then it is issued here, with the clamped offsets)
-        const bool dma_il = do_dma && (!FAST || dt.kmax >= wkey);  // wave-uniform
-        if (!last && do_dma && !dma_il) dma_all(dt);
+        const bool dma_il = !FP8 && do_dma && (!FAST || dt.kmax >= wkey);  // wave-uniform
+        if (!FP8 && !last && do_dma && !dma_il) dma_all(dt);
+        if (FP8 && !last && widen_next) raw_ready();
         // ---- S^T[32 keys][32 rows] = K . Q^T: 36 k-steps over the 576 dims, with this
         // wave's DMA of a later tile between the MFMAs ----
         if (!last) {
           const char* kp = smem + qst + kbase;
           auto k_at = [&](int k) __attribute__((always_inline)) { return *(const u32x4_t*)(kp + 32 * k); };
-          constexpr int KR = 4;  // K fragment ring depth
+          constexpr int KR = KRING;
           u32x4_t kb[KR];
 #pragma unroll
           for (int k = 0; k < KR; ++k) kb[k] = k_at(k);
+          // the first DMA steps fill the wait for the first K fragments
+          if constexpr (!FP8)
+            static_for<DMA0>([&](auto nc) __attribute__((always_inline)) {
+              if (dma_il) dma_one(dt, nc);
+            });
           static_for<36>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             if constexpr (k == 0)
@@ -957,8 +1071,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
             else
               mfma_acc_v(sc, kb[k % KR], qr[k]);
             if constexpr (k + KR < 36) kb[k % KR] = k_at(k + KR);
-            if constexpr (k % 3 == 2 && k / 3 < 10) {
-              if (dma_il) dma_one(dt, std::integral_constant<int, k / 3>{});
+            constexpr int n = DMA0 + k / 3;
+            if constexpr (!FP8 && k % 3 == 2 && n < 10) {
+              if (dma_il) dma_one(dt, std::integral_constant<int, n>{});
+            }
+            // fp8: widen this wave's rows of tile s+1, then load raw tile s+3 into their slot
+            if constexpr (FP8 && k >= 2 && k % 3 == 2 && k / 3 < 9) {
+              if (widen_next) widen(raw_slot(g + 1), wst, std::integral_constant<int, k / 3>{});
+            }
+            if constexpr (FP8 && k == 30) {
+              if (do_dma) dma_raw(dt);
             }
           });
         }
@@ -1073,13 +1195,22 @@ __global__ __launch_bounds__(256, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
             acc_written(O[cb]);
           }
         }
-      } else if (do_dma) {
-        dma_all(dt);
+      } else {
+        if constexpr (FP8) {
+          if (widen_next) {
+            raw_ready();
+            static_for<9>([&](auto ic) __attribute__((always_inline)) { widen(raw_slot(g + 1), wst, ic); });
+          }
+          if (do_dma) dma_raw(dt);
+        } else {
+          if (do_dma) dma_all(dt);
+        }
       }
       if (do_dma) {
         pf = next_tile(segs, pf, s_end);
         issued++;
       }
+      if (widen_next) widened++;
     }
     done = g0 + nt;
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // the last P.V MFMA's result is read next
@@ -1150,13 +1281,14 @@ hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
   const dim3 grid(parts8 * a.head_groups);
   const bool p32 = (a.page_size % 32) == 0;
   if (fp8) {
-    if (p32) launch_nrb<true, true>(a, nrb, grid, stream);
-    else launch_nrb<true, false>(a, nrb, grid, stream);
+    const bool canon = (const char*)a.k_pe == (const char*)a.kv_c + kLkv;
+    if (p32 && canon) hipLaunchKernelGGL((mla_decode_pipe_kernel<true, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_pipe_kernel<false, true>), grid, dim3(256), 0, stream, a);
   } else {
     // one base for the whole cache row: the rope columns follow the latent ones
     const bool canon = (const char*)a.k_pe == (const char*)a.kv_c + 2 * kLkv;
-    if (p32 && canon) hipLaunchKernelGGL((mla_decode_bf16_kernel<true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_bf16_kernel<false>), grid, dim3(256), 0, stream, a);
+    if (p32 && canon) hipLaunchKernelGGL((mla_decode_pipe_kernel<true, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_pipe_kernel<false, false>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
