@@ -5,40 +5,19 @@
 // docstring, "Data-Movement Friendly Approach"): an MQA whose single KV head is the
 // 576-wide latent row, shared by all Sq*N query rows of the request.
 //
-// Work split.  One workgroup (4 waves) per (plan part, head group of up to 128
-// query rows, NRB = ceil(rows / 32) row blocks).  Per tile of 32 keys:
-//  QK^T     wave w < NRB computes S^T = K.Q^T for rows 32w..32w+31 (its query rows
-//           stay in VGPRs for the whole segment), then the softmax of those rows,
-//           and writes P (bf16) and the rows' rescale factors to LDS.
-//  P.V      after a barrier, wave w accumulates O^T += V^T.P^T for output columns
-//           128w..128w+127 of every row of the group: 4 x NRB accumulator blocks
-//           (up to all 256 AGPRs), reading only its quarter of the value tile.
-// The head groups of one part are dealt to one XCD, so when Sq*N > 128 a tile that
-// one group reads from HBM reaches the others from that XCD's L2.
-//
-// Tiles.  A tile is 32 cache rows.  A bf16 stage in LDS holds the latent part
-// [32][512] (1 KB rows) and the rope part [32][64], each with an XOR swizzle of its
-// 16-byte chunks that keeps the QK reads (ds_read_b128) and the transposing V reads
-// (ds_read_b64_tr_b16) free of bank conflicts.
-//  bf16 cache: HBM -> LDS with global_load_lds_dwordx4 (no VGPRs); 4 stages, the
-//    tile being computed plus up to 3 in flight.
-//  fp8 cache: raw e4m3 tiles go HBM -> LDS the same way (4 raw stages of 18 KB) and
-//    are widened one tile ahead of the compute into 2 bf16 stages with
-//    v_cvt_scalef32_pk_bf16_fp8 (every e4m3 value is exact in bf16).
-//  Keys past a segment end load a valid key instead and get probability 0, so
-//  unused page slots and block_table entries are never read.
-//
-// Softmax.  fp32, log2 domain.  Each row keeps a reference maximum m, and p =
-// 2^(c s - m) is accumulated without touching O while the tile maxima stay within
-// 2^8 of m.  A tile that goes further raises m to its maximum; the row's running sum
-// is rescaled by the QK wave and its O columns by every wave, with the factor passed
-// through LDS next to P (rare after the first tile of a segment).
+// Work split.  One workgroup (4 waves, one per SIMD) per (plan part, head group of up
+// to 128 query rows).  Wave w owns query rows 32w..32w+31: their queries stay in VGPRs
+// for a whole segment, O (32 rows x 512 columns, fp32) in the 256 AGPRs.  Only the key
+// tile (32 cache rows) is shared, through LDS.  The head groups of one part are dealt to
+// one XCD, so when Sq*N > 128 a tile one group reads from HBM reaches the others from
+// that XCD's L2.  The pipelined step loop and the stage layout are described with the
+// kernel below.
 //
 // MFMAs (v_mfma_f32_32x32x16_bf16) are inline asm: only then does the compiler leave
-// all accumulation registers to O.  It does not model MFMA hazards across inline
-// asm, so each statement carries its own wait states: 3 before an MFMA whose
-// operands a VALU may just have written, 16 after the last MFMA of a chain whose
-// result is read next (the compiler itself pads 1-2 and 12 on gfx950).
+// all accumulation registers to O.  It does not model MFMA hazards across inline asm,
+// so the statements carry their own wait states where a VALU result or read is near:
+// 3 before an MFMA whose operands a VALU may just have written, 16 after the last MFMA
+// of a chain whose result is read next (the compiler itself pads 1-2 and 12 on gfx950).
 #include <utility>
 
 #include "common.h"
@@ -50,37 +29,21 @@ namespace mla {
 
 namespace {
 
-constexpr int kTile = 32;
-constexpr int kLatRow = kLkv * 2;                         // 1024: latent part of a bf16 row
-constexpr int kRopeRow = kRope * 2;                       // 128: rope part
-constexpr int kRopeOff = kTile * kLatRow;                 // 32768: rope part of a stage
-constexpr int kStageBytes = kRopeOff + kTile * kRopeRow;  // 36864
-constexpr int kStages = 4;                                // bf16 cache
-constexpr int kRawRopeOff = kTile * kLkv;                 // 16384: rope part of a raw fp8 stage
-constexpr int kRawBytes = kRawRopeOff + kTile * kRope;    // 18432
-constexpr int kRawStages = 4;                             // fp8 cache (plus 2 bf16 stages)
-constexpr int kRawOff = 2 * kStageBytes;                  // 73728
-constexpr int kStageArea = kStages * kStageBytes;         // 147456
-static_assert(kRawOff + kRawStages * kRawBytes == kStageArea, "fp8 stages fill the bf16 layout");
-constexpr int kPOff = kStageArea;                         // P [128 rows][32 keys] bf16, 64 B rows
-constexpr int kFacOff = kPOff + kGroupRows * 64;          // per-row rescale factor of the tile
-constexpr int kEllOff = kFacOff + kGroupRows * 4;         // per-row sums for the epilogue
-constexpr int kSmemBytes = kEllOff + kGroupRows * 4;      // 156672
+constexpr int kTile = 32;                    // keys per tile
+constexpr int kStages = 4;                   // bf16 stages (bf16 caches)
+constexpr int kRowB = 1168;                  // LDS bytes per key row (576 bf16 + 16 pad)
+constexpr int kRowC = kRowB / 16;            // 73 chunks
+constexpr int kStageB = kTile * kRowB;       // 37376
+constexpr int kStageC = kTile * kRowC;       // 2336
+constexpr int kDmaN = (kStageC + 63) / 64;   // 37 DMA instructions per tile
+static_assert(kDmaN == 37, "the last DMA instruction of a tile is the only partial one");
+constexpr int kSmemBytes = kStages * kStageB;  // 149504
 constexpr float kRescaleAt = 8.f;  // log2 units a tile maximum may exceed the reference by
 
 __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
-
-// The lane index, produced by a volatile instruction pair so that per-lane values
-// derived from it are recomputed where they are used instead of being hoisted out
-// of the loops and kept live (VGPRs are the scarce resource of this kernel).
-__device__ __forceinline__ int lane_id() {
-  int v;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
-  return v;
-}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_char*)p;
@@ -90,12 +53,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 64-bit per-lane address.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr),
-               "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
-}
-// Same, with a wave-uniform 64-bit base and a 32-bit per-lane byte offset.
-__device__ __forceinline__ void dma16_s(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase),
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
@@ -124,22 +81,11 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // ---- MFMA statements (see the header for the wait states) ----
-__device__ __forceinline__ void mfma_first(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
 __device__ __forceinline__ void mfma_acc_v(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_acc_v_last(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_acc_a(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_acc_a_last(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(d)
-               : "v"(a), "v"(b));
 }
 // Orders VALU writes of an accumulator before the next MFMA that reads it.
 __device__ __forceinline__ void acc_written(f32x16_t& d) { asm volatile("s_nop 2" : "+a"(d)); }
@@ -159,28 +105,6 @@ __device__ __forceinline__ void acc_zero(f32x16_t (&o)[NB]) {
 // Keeps an accumulator in AGPRs up to this point, so that the compiler copies it to
 // VGPRs only where it is read, one block at a time (not all 256 registers at once).
 __device__ __forceinline__ void acc_fence(f32x16_t& d) { asm volatile("" : "+a"(d)::"memory"); }
-
-// LDS swizzles (64 banks of 4 bytes: a 16-byte chunk's bank group is its index mod 16).
-// Latent rows are 1 KB apart, so every row starts in the same bank group; logical chunk
-// c of key k sits in physical chunk c ^ lat_swz(k).  lat_swz is a bijection on k & 15,
-// so the 16 keys of one ds_read_b128 cycle (same c) hit 16 distinct bank groups, and for
-// any 4 consecutive keys 4a..4a+3 it gives 4 distinct chunk pairs, so the transposing
-// V reads (4 keys x 2 chunks per 16-lane group) are conflict-free too.
-__device__ __forceinline__ int lat_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
-// Rope rows are 128 B (8 chunks): keys 2m and 2m+1 share bank groups 0..7 / 8..15, so
-// the keys of one parity need distinct chunks.
-__device__ __forceinline__ int rope_swz(int k) { return (k >> 1) & 7; }
-
-// P row r holds keys in 4 chunks of 16 bytes; chunk q sits at q ^ ((r >> 2) & 3), so the
-// 16 rows of one 16-lane access (same q) cover all 16 bank groups.
-__device__ __forceinline__ int p_off(int r, int q) { return kPOff + r * 64 + ((q ^ ((r >> 2) & 3)) << 4); }
-
-// Byte offset in a bf16 stage of logical 16-byte chunk c (0..71) of key row `key`: the
-// latent row (c < 64) or the rope row (c >= 64), swizzled as above.
-__device__ __forceinline__ int tile_off(int key, int c) {
-  return c < 64 ? key * kLatRow + ((c ^ lat_swz(key)) << 4)
-                : kRopeOff + key * kRopeRow + (((c - 64) ^ rope_swz(key)) << 4);
-}
 
 struct Seg {
   int b, ks, ke, pidx;
@@ -238,95 +162,8 @@ __device__ __forceinline__ DmaTile dma_tile(const DecodeArgs& a, const Cursor& p
   return t;
 }
 
-// Number of dma_issue steps per tile (the DMA instruction count per wave is PER).
-template <bool FP8>
-constexpr int kDmaSteps = FP8 ? 5 : 9;
-
-// Step i of this wave's DMA of tile t.  Keys past the segment end load key kmax instead.
-// bf16: steps 0..7 load latent row 8w+i (lane = physical chunk), step 8 the rope parts of
-//   rows 8w..8w+7 (lane = 8 rows x 8 chunks; 8 row-wise instructions when rows may sit on
-//   different pages).
-// fp8 (raw stage: latent [32][512] then rope [32][64] bytes, unswizzled): steps 0..3 load
-//   latent rows 8w+2i, 8w+2i+1 (lane = key half, 16-byte piece), step 4 the rope parts of
-//   rows 8w..8w+7 on lanes 0..31 (lane = row 8w + lane/4, piece lane%4).
-template <bool FP8, bool PAGED32>
-__device__ __forceinline__ void dma_issue(const DecodeArgs& a, const DmaTile& t, int i, int w, int lane) {
-  if constexpr (!FP8) {
-    const uint32_t st = (uint32_t)a.s_tok * 2;
-    const uint32_t l16 = (uint32_t)lane << 4;
-    if (i < 8) {
-      const int key = 8 * w + i;  // wave-uniform
-      const int kc = min(key, t.kmax);
-      if constexpr (PAGED32) {
-        dma16_s(t.kv, (uint32_t)kc * st + (l16 ^ (uint32_t)(lat_swz(key) << 4)), t.lds + key * kLatRow);
-      } else {
-        dma16_s(t.kv + row_bytes(a, t.bt_row, t.ts + kc, 2), l16 ^ (uint32_t)(lat_swz(key) << 4),
-                t.lds + key * kLatRow);
-      }
-    } else {
-      const uint32_t rlds = t.lds + kRopeOff + 8 * w * kRopeRow;
-      if constexpr (PAGED32) {
-        const int rk = 8 * w + (lane >> 3);
-        const uint32_t kc = (uint32_t)min(rk, t.kmax);
-        dma16_s(t.pe, kc * st + ((((uint32_t)lane & 7) ^ (uint32_t)rope_swz(rk)) << 4), rlds);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int key = 8 * w + r;
-          const int64_t roff = row_bytes(a, t.bt_row, t.ts + min(key, t.kmax), 2);
-          if ((lane >> 3) == r)
-            dma16_s(t.pe + roff, (((uint32_t)lane & 7) ^ (uint32_t)rope_swz(key)) << 4, rlds);
-        }
-      }
-    }
-  } else {
-    const uint32_t st = (uint32_t)a.s_tok;
-    if (i < 4) {
-      const int k0 = 8 * w + 2 * i;  // wave-uniform; this lane's key is k0 + lane/32
-      const uint32_t l16 = 16u * ((uint32_t)lane & 31);
-      if constexpr (PAGED32) {
-        const uint32_t kc = (uint32_t)min(k0 + (lane >> 5), t.kmax);
-        dma16_s(t.kv, kc * st + l16, t.lds + k0 * kLkv);
-      } else {
-        const int64_t r0 = row_bytes(a, t.bt_row, t.ts + min(k0, t.kmax), 1);
-        const int64_t r1 = row_bytes(a, t.bt_row, t.ts + min(k0 + 1, t.kmax), 1);
-        dma16(t.kv + ((lane >> 5) ? r1 : r0) + l16, t.lds + k0 * kLkv);
-      }
-    } else {
-      const uint32_t rlds = t.lds + kRawRopeOff + 8 * w * kRope;
-      if constexpr (PAGED32) {
-        const uint32_t kc = (uint32_t)min(8 * w + (lane >> 2), t.kmax);
-        if (lane < 32) dma16_s(t.pe, kc * st + 16u * ((uint32_t)lane & 3), rlds);
-      } else {
-        int64_t rb = 0;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int64_t ro = row_bytes(a, t.bt_row, t.ts + min(8 * w + r, t.kmax), 1);
-          if ((lane >> 2) == r) rb = ro;
-        }
-        if (lane < 32) dma16(t.pe + rb + 16 * (lane & 3), rlds);
-      }
-    }
-  }
-}
-
-// fp8: widens raw tile `raw` into bf16 stage `stage` (all 256 threads; 2304 pieces of
-// 8 values, 9 per thread).
-__device__ __forceinline__ void convert_fp8_tile(const char* raw, char* stage, int tid) {
-#pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    const int u = tid + 256 * i;
-    const int key = u / 72, c = u - 72 * key;
-    const int src = c < 64 ? key * kLkv + 8 * c : kRawRopeOff + key * kRope + 8 * (c - 64);
-    const u32x2_t v = *(const u32x2_t*)(raw + src);
-    const u32x2_t lo = fp8x4_to_bf16x4(v[0]);
-    const u32x2_t hi = fp8x4_to_bf16x4(v[1]);
-    *(u32x4_t*)(stage + tile_off(key, c)) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-  }
-}
-
 // 8 bf16 of V^T (column of this lane, 8 keys) from the row-major tile: two transposing
-// reads, p0 for keys t0..t0+3 and p1 for keys t0+8..t0+11.
+// reads of 4 keys each (p0: elements 0..3 of the MFMA operand, p1: elements 4..7).
 __device__ __forceinline__ u32x4_t read_vt(const char* p0, const char* p1) {
   const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)p0);
@@ -336,365 +173,21 @@ __device__ __forceinline__ u32x4_t read_vt(const char* p0, const char* p1) {
   return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
 }
 
-// LDS target of the next tile to issue (bf16 stage or raw fp8 stage).
-template <bool FP8>
-__device__ __forceinline__ uint32_t next_lds(int issued) {
-  return FP8 ? lds_addr(smem + kRawOff) + (issued % kRawStages) * kRawBytes
-             : lds_addr(smem) + (issued % kStages) * kStageBytes;
-}
-
-// Issues the whole next tile at the cursor, if any (pipeline prologue).
-template <bool FP8, bool PAGED32>
-__device__ __forceinline__ void issue_next(const DecodeArgs& a, const int32_t* segs, int s_end, Cursor& pf,
-                                           int& issued, int w) {
-  if (pf.si >= s_end) return;
-  const DmaTile t = dma_tile<FP8, PAGED32>(a, pf, next_lds<FP8>(issued));
-#pragma unroll
-  for (int i = 0; i < kDmaSteps<FP8>; ++i) dma_issue<FP8, PAGED32>(a, t, i, w, lane_id());
-  pf = next_tile(segs, pf, s_end);
-  issued++;
-}
-
 }  // namespace
 
-template <bool FP8, bool PAGED32, int NRB>
-__global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
-  constexpr int PER = FP8 ? 5 : (PAGED32 ? 9 : 16);  // DMA instructions per wave per tile
-  constexpr int NB = 4 * NRB;                          // accumulator blocks per wave
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
-
-  // Workgroups are dealt round-robin to the 8 XCDs; keep the head groups of
-  // one part on one XCD so that they share its L2 for the part's keys.
-  const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
-  const int hg = slot % a.head_groups;
-  const int part = xcd + 8 * (slot / a.head_groups);
-  if (part >= a.num_parts) return;
-
-  const int R = a.Sq * a.N;
-  const int row0 = hg * kGroupRows;
-  const int RG = min(kGroupRows, R - row0);  // rows of this group, <= 32 NRB
-  const bool qk_wave = w < NRB;              // wave-uniform: owns query rows 32w..32w+31
-  const int32_t* segs = a.segs;
-  const int s_beg = ld_uniform(a.part_begin + part), s_end = ld_uniform(a.part_begin + part + 1);
-  float* fac_l = (float*)(smem + kFacOff);
-  float* ell_l = (float*)(smem + kEllOff);
-
-  // ---- load pipeline (wave-uniform state) ----
-  Cursor pf = first_tile(segs, s_beg, s_end);  // next tile to load
-  int issued = 0, consumed = 0;
-  if constexpr (FP8) {
-    for (int k = 0; k < kRawStages; ++k) issue_next<FP8, PAGED32>(a, segs, s_end, pf, issued, w);
-    if (issued > 0) {
-      wait_tiles<PER>(issued - 1);
-      barrier_lds();
-      convert_fp8_tile(smem + kRawOff, smem, 64 * w + lane_id());
-    }
-  } else {
-    for (int k = 0; k < kStages - 1; ++k) issue_next<FP8, PAGED32>(a, segs, s_end, pf, issued, w);
-  }
-
-  for (int si = s_beg; si < s_end; ++si) {
-    const Seg sg = load_seg(segs, si);
-    const int b = sg.b, ks = sg.ks, ke = sg.ke, pidx = sg.pidx;
-    const int L = ld_uniform(a.seq_lens + b);
-
-    // Query rows of a QK wave: B operand of S^T = K . Q^T, 36 x 8 bf16 per lane
-    // (lane: row 32w + l%32, dims 16k + 8(l/32) .. +7 of k-step k).
-    u32x4_t qr[36];
-    int lim = ke;  // keys j < lim are visible to this lane's row (segment end, causal window)
-    if (qk_wave) {
-      const int ql = lane_id(), rl = 32 * w + (ql & 31), qh = ql >> 5;
-      if (rl < RG) {
-        const int r = row0 + rl;
-        const int t = r / a.N, h = r - t * a.N;
-        const int64_t tok = (int64_t)b * a.Sq + t;
-        const uint16_t* qn = a.q_nope + tok * a.q_nope_s_tok + (int64_t)h * a.q_nope_s_head + 8 * qh;
-        const uint16_t* qp = a.q_pe + tok * a.q_pe_s_tok + (int64_t)h * a.q_pe_s_head + 8 * qh;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) qr[k] = *(const u32x4_t*)(qn + 16 * k);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) qr[32 + k] = *(const u32x4_t*)(qp + 16 * k);
-        lim = min(ke, L - (a.Sq - 1) + t);
-      } else {
-        // padding rows: zero queries give zero logits; their probabilities only reach
-        // output rows that are never stored
-#pragma unroll
-        for (int k = 0; k < 36; ++k) qr[k] = u32x4_t{0, 0, 0, 0};
-      }
-      // A wait the compiler sees: the query loads are complete before the tile loop,
-      // so it places no vmcnt waits there (those would also count the DMA loads in
-      // flight and drain the prefetch pipeline).  s_waitcnt vmcnt(0).
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-
-    float m_ref = -INFINITY;  // reference maximum of this lane's row (log2 units)
-    float l_acc = 0.f;        // running sum over this lane's 16 keys of each tile
-    f32x16_t O[NB];           // O^T[32 cols of block cb][32 rows of block rb] at [cb * NRB + rb]
-    acc_zero<NB>(O);
-
-    for (int ts = ks; ts < ke; ts += kTile) {
-      // ---- pipeline: wait for this tile, describe the next DMA, barrier ----
-      const bool do_dma = pf.si < s_end;  // wave-uniform
-      const char* stage;
-      bool cvt_next = false;
-      if constexpr (FP8) {
-        // raw tile consumed+1 (if any) must have landed for every wave before it is widened
-        cvt_next = consumed + 1 < issued;
-        if (cvt_next) wait_tiles<PER>(issued - consumed - 2);
-        stage = smem + (consumed & 1) * kStageBytes;
-      } else {
-        wait_tiles<PER>(issued - consumed - 1);  // this wave's part of the tile has landed
-        stage = smem + (consumed % kStages) * kStageBytes;
-      }
-      DmaTile dt{};
-      if (do_dma) dt = dma_tile<FP8, PAGED32>(a, pf, next_lds<FP8>(issued));
-      // every wave's part has landed; the stage issued into next and P are free
-      barrier_lds();
-      if constexpr (FP8) {
-        if (cvt_next)
-          convert_fp8_tile(smem + kRawOff + ((consumed + 1) % kRawStages) * kRawBytes,
-                           smem + ((consumed + 1) & 1) * kStageBytes, 64 * w + lane_id());
-      }
-
-      // V^T fragments of this wave's columns for both k-steps (see the PV step below).
-      // Requested before the softmax so that they arrive while it runs.
-      u32x4_t vt[2][4];
-      auto load_vt = [&]() {
-        const int pl = lane_id(), ph = pl >> 5, g = pl >> 4, j = pl & 15;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          int off[2];
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            const int key = 4 * ph + (j >> 2) + 8 * kh;
-            const int col = 128 * w + 32 * cb + 16 * (g & 1) + 4 * (j & 3);
-            off[kh] = key * kLatRow + (((col >> 3) ^ lat_swz(key)) << 4) + 8 * ((col >> 2) & 1);
-          }
-#pragma unroll
-          for (int sk = 0; sk < 2; ++sk)
-            vt[sk][cb] = read_vt(stage + off[0] + 16 * kLatRow * sk, stage + off[1] + 16 * kLatRow * sk);
-        }
-      };
-
-      if (qk_wave) {
-        // ---- S^T[32 keys][32 rows] = K . Q^T: 36 k-steps over the 576 dims ----
-        // A operand: key r32, logical chunk 2k + h2 at kq_off[k & 7] + 256 (k >> 3)
-        // (latent, k < 32; the swizzle permutes chunks within a 16-chunk group) or
-        // kr_off[k - 32] (rope).  K fragments stream through an 8-deep ring; the DMA of
-        // the next tile is spread over the chain, one step after every fourth MFMA.
-        f32x16_t sacc;
-        const int ln = lane_id(), r32 = ln & 31, h2 = ln >> 5;
-        {
-          int kq_off[8], kr_off[4];
-#pragma unroll
-          for (int m = 0; m < 8; ++m) kq_off[m] = r32 * kLatRow + (((2 * m + h2) ^ lat_swz(r32)) << 4);
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            kr_off[m] = kRopeOff + r32 * kRopeRow + (((2 * m + h2) ^ rope_swz(r32)) << 4);
-          auto k_at = [&](int k) {
-            return *(const u32x4_t*)(stage + (k < 32 ? kq_off[k & 7] + 256 * (k >> 3) : kr_off[k - 32]));
-          };
-          u32x4_t kb[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) kb[k] = k_at(k);
-#pragma unroll
-          for (int k = 0; k < 36; ++k) {
-            if (k == 0)
-              mfma_first(sacc, kb[0], qr[0]);
-            else if (k == 35)
-              mfma_acc_v_last(sacc, kb[k & 7], qr[k]);
-            else
-              mfma_acc_v(sacc, kb[k & 7], qr[k]);
-            if (k + 8 < 36) kb[k & 7] = k_at(k + 8);
-            if ((k & 3) == 3 && (k >> 2) < kDmaSteps<FP8> && do_dma)
-              dma_issue<FP8, PAGED32>(a, dt, k >> 2, w, lane_id());
-          }
-        }
-        load_vt();
-
-        // ---- softmax (lane: row 32w + l%32, keys ts + 8(v/4) + 4 h2 + v%4) ----
-        const float c = a.qk_scale_log2;
-        if (!__all(ts + kTile <= lim)) {
-          const int rem = lim - ts - 4 * h2;
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (8 * (v >> 2) + (v & 3) >= rem) sacc[v] = -INFINITY;
-        }
-        float mx = sacc[0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-        mx = half_max(mx) * c;
-        float fac = 1.f;  // factor for this row's O and sum (applied by every wave)
-        if (__any(mx > m_ref + kRescaleAt)) {
-          if (__all(m_ref == -INFINITY)) {
-            m_ref = mx;  // first keys of the segment: O and the sums are still zero
-          } else {
-            const float m_new = fmaxf(m_ref, mx);
-            fac = (m_new > m_ref) ? fast_exp2(m_ref - m_new) : 1.f;
-            l_acc *= fac;
-            m_ref = m_new;
-          }
-        }
-        // exp2(-inf) = 0 covers masked keys; rows without a visible key yet keep m = -inf
-        const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
-        uint32_t pk[8];
-        float psum = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const float p0 = fast_exp2(fmaf(sacc[v], c, nm));
-          const float p1 = fast_exp2(fmaf(sacc[v + 1], c, nm));
-          psum += p0 + p1;
-          pk[v >> 1] = pack_bf16x2(p0, p1);
-        }
-        l_acc += psum;
-        // P chunk q = 2s + h2 of row 32w + r32 holds keys 16s + 4 h2 + (e & 3) + 8 (e >> 2)
-        const int prow = 32 * w + r32;
-        *(u32x4_t*)(smem + p_off(prow, h2)) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-        *(u32x4_t*)(smem + p_off(prow, 2 + h2)) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
-        if (h2 == 0) fac_l[prow] = fac;
-      } else {
-        if (do_dma) {
-#pragma unroll
-          for (int i = 0; i < kDmaSteps<FP8>; ++i) dma_issue<FP8, PAGED32>(a, dt, i, w, lane_id());
-        }
-        load_vt();
-      }
-      if (do_dma) {
-        pf = next_tile(segs, pf, s_end);
-        issued++;
-      }
-      barrier_lds();  // P and the factors of every row are in LDS
-
-      // ---- rescale (rare): O rows whose reference maximum was raised this tile ----
-      {
-        const int fl = lane_id() & 31;
-        float f[NRB];
-        bool any = false;
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          f[rb] = fac_l[32 * rb + fl];
-          any |= f[rb] != 1.f;
-        }
-        if (__any(any)) {
-#pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            acc_fence(O[i]);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) O[i][v] *= f[i % NRB];
-            acc_written(O[i]);
-          }
-        }
-      }
-
-      // ---- O^T[cols 128w + 32cb ..][rows 32rb ..] += V^T . P^T, 16 keys per k-step ----
-      // B operand (P^T): row 32rb + l%32, logical keys 8(l/32) + e of k-step s = chunk
-      // 2s + l/32 of the P row.  A operand (V^T) through ds_read_b64_tr_b16: 16-lane
-      // group g covers columns 128w + 32cb + 16(g & 1) + 0..15 and keys t0..t0+3
-      // (t0 = 16s + 4(g >> 1), +8 for the second read); lane j addresses key t0 + j/4 at
-      // columns +4(j & 3) and receives keys t0..t0+3 of column +j.
-      {
-        const int pl = lane_id(), p32 = pl & 31, ph = pl >> 5;
-        u32x4_t pf4[2][NRB];
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-          for (int rb = 0; rb < NRB; ++rb)
-            pf4[sk][rb] = *(const u32x4_t*)(smem + p_off(32 * rb + p32, 2 * sk + ph));
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) {
-              if (sk == 1 && cb == 3 && rb == NRB - 1)
-                mfma_acc_a_last(O[cb * NRB + rb], vt[sk][cb], pf4[sk][rb]);
-              else
-                mfma_acc_a(O[cb * NRB + rb], vt[sk][cb], pf4[sk][rb]);
-            }
-      }
-      consumed++;
-    }
-
-    // ---- epilogue: o = O * kv_scale / l, lse = ln(sum exp) ----
-    if (qk_wave) {
-      const float l_row = half_sum(l_acc);
-      const int el = lane_id();
-      const int rl = 32 * w + (el & 31);
-      if (el < 32) ell_l[rl] = l_row;
-      if (el < 32 && rl < RG) {
-        const int r = row0 + rl;
-        const float lse = (l_row > 0.f) ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
-        const int t = r / a.N, h = r - t * a.N;
-        if (pidx < 0) {
-          if (a.lse) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
-        } else {
-          a.ws_lse[(int64_t)pidx * R + r] = lse;
-          a.ws_l[(int64_t)pidx * R + r] = l_row / a.out_scale;
-        }
-      }
-    }
-    barrier_lds();  // row sums of every row are in LDS
-    {
-      const int el = lane_id(), e32 = el & 31, eh = el >> 5;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const int rl = 32 * rb + e32;
-        if (rl >= RG) continue;
-        const int r = row0 + rl;
-        const float lsum = ell_l[rl];
-        const float f = (lsum > 0.f) ? a.out_scale / lsum : 0.f;
-        const int t = r / a.N, h = r - t * a.N;
-        if (pidx < 0) {
-          uint16_t* orow = a.o + ((int64_t)b * a.Sq + t) * a.o_s_tok + (int64_t)h * a.o_s_head;
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            f32x16_t& acc = O[cb * NRB + rb];
-            acc_fence(acc);
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int col = 128 * w + 32 * cb + 8 * gq + 4 * eh;
-              u32x2_t pk2;
-              pk2[0] = pack_bf16x2(acc[4 * gq] * f, acc[4 * gq + 1] * f);
-              pk2[1] = pack_bf16x2(acc[4 * gq + 2] * f, acc[4 * gq + 3] * f);
-              *(u32x2_t*)(orow + col) = pk2;
-            }
-          }
-        } else {
-          // unnormalised partial block of rows row0 + 32rb .. +31 (the reduce divides by
-          // the stored row sums), in accumulator order: chunk q = 4 (32-column block) + gq
-          // holds 64 lanes x 4 floats (lane: row e32, columns 8 gq + 4 eh .. +3 of the
-          // block), so each store is 1 KB contiguous, straight from the AGPRs
-          float* pblk = a.ws_o + ((int64_t)pidx * partial_rows(a.Sq, a.N) + row0 + 32 * rb) * kLkv;
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            f32x16_t& acc = O[cb * NRB + rb];
-            acc_fence(acc);
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int q = 4 * (4 * w + cb) + gq;
-              *(f32x4_t*)(pblk + 4 * (64 * q + el)) = f32x4_t{acc[4 * gq], acc[4 * gq + 1], acc[4 * gq + 2], acc[4 * gq + 3]};
-            }
-          }
-        }
-      }
-    }
-  }
-  wait_vm<0>();  // no DMA outlives the workgroup
-}
-
 // ---------------------------------------------------------------------------------
-// Software-pipelined kernel for bf16 caches.  Wave w owns query rows 32w..32w+31 from
-// end to end: Q in VGPRs, O (all 512 columns) in the 256 AGPRs and P in VGPRs, so only
-// the key tile is shared.  Step s of a segment of n tiles (s = 0..n):
+// Software-pipelined decode kernel.  Wave w owns query rows 32w..32w+31 from end to end:
+// Q in VGPRs, O (all 512 columns) in the 256 AGPRs and P in VGPRs, so only the key tile
+// is shared.  Step s of a segment of n tiles (s = 0..n):
 //   wait for tile s, barrier;
 //   QK of tile s (36 MFMAs), with this wave's DMA of a later tile between its MFMAs;
 //   P.V of tile s-1 (32 MFMAs), with the softmax of tile s between them;
 //   rescale of O when tile s raised a row's reference maximum (rare).
 // One loop body serves every step, so O stays in one set of registers: step 0 runs its
-// P.V with P = 0 against the landed tile 0, and step n a QK against tile n-1 whose
-// result is discarded (every key masked).  A stage is
-// reloaded once the P.V of the tile it held is complete, two steps before its QK.
+// P.V with P = 0 against the landed tile 0, and step n has no QK (its softmax sees every
+// key masked).  A stage is reloaded once the P.V of the tile it held is complete, two
+// steps before its QK.  fp8 caches add a widening of each tile to bf16 one step ahead
+// (see the fp8 ring below).
 // With one wave per SIMD every instruction takes an issue slot of the MFMA stream, so
 // the per-tile address and bookkeeping work is kept small.
 //
@@ -712,13 +205,6 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(DecodeArgs a) {
 // the pads receiving a copy of a neighbouring chunk.
 // ---------------------------------------------------------------------------------
 
-constexpr int kRowB = 1168;                  // LDS bytes per key row (576 bf16 + 16 pad)
-constexpr int kRowC = kRowB / 16;            // 73 chunks
-constexpr int kStageB = kTile * kRowB;       // 37376
-constexpr int kStageC = kTile * kRowC;       // 2336
-constexpr int kDmaN = (kStageC + 63) / 64;   // 37 DMA instructions per tile
-static_assert(kStages * kStageB <= kSmemBytes, "bf16 stages fit");
-static_assert(kDmaN == 37, "the last DMA instruction of a tile is the only partial one");
 
 // Calls f(std::integral_constant<int, K>) for K = 0..N-1 in order, as straight-line code.
 template <int N, typename F>
@@ -1263,20 +749,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   wait_vm<0>();  // no DMA outlives the workgroup
 }
 
-template <bool FP8, bool PAGED32>
-static void launch_nrb(const DecodeArgs& a, int nrb, dim3 grid, hipStream_t stream) {
-  switch (nrb) {
-    case 1: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 1>), grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 2>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((mla_decode_kernel<FP8, PAGED32, 4>), grid, dim3(256), 0, stream, a); break;
-  }
-}
-
 hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
-  // Every head group but the last has 128 rows; the last may be smaller, but a group
-  // never needs more row blocks than the first one, so one instance serves all.
-  const int R = a.Sq * a.N;
-  const int nrb = (min(R, kGroupRows) + 31) / 32;
   const int parts8 = (a.num_parts + 7) / 8 * 8;
   const dim3 grid(parts8 * a.head_groups);
   const bool p32 = (a.page_size % 32) == 0;
