@@ -239,8 +239,22 @@ def main():
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t0
     ms_per_step = t_total / K * 1e3
-    dec_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
-    red_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    # Kernel durations: K back-to-back launches between two events on the launch stream
+    # (per-step events would also count the launch gap in front of each kernel).  The
+    # reduce only reads the partial states, so repeating it is the same work each time.
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e3
+    dec_us = timed(lambda: api.mla_decode_attend(plan, ql, q_pe, cache, bt, sl, w.scale, inp.kv_scale,
+                                                 o_lat, lse, ws))
+    red_us = timed(lambda: api.mla_decode_reduce(plan, o_lat, lse, ws))
+    step_dec_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
 
     # Cold-cache timing of the decode kernel: a 1 GiB write evicts L2 and the 256 MB MALL.
     cold_us = None
@@ -281,6 +295,7 @@ def main():
                    "lse": with_lse},
         "roofline": roof,
         "decode_kernel_us": round(dec_us, 2), "reduce_kernel_us": round(red_us, 2),
+        "decode_in_step_us": round(step_dec_us, 2),
         "decode_kernel_cold_us": None if cold_us is None else round(cold_us, 2),
         "hbm_gbps": round(hbm_gbs, 1), "tflops": round(tflops, 1),
         "frac_hbm": round(hbm_gbs / HBM_PEAK_GBS, 4), "frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),
