@@ -93,14 +93,30 @@ __device__ __forceinline__ void acc_written(f32x16_t& d) { asm volatile("s_nop 2
 // zero vector in VGPRs that the compiler would keep live across the loops.
 template <int NB>
 __device__ __forceinline__ void acc_zero(f32x16_t (&o)[NB]) {
-  u32x4_t z = u32x4_t{0, 0, 0, 0};
-  asm volatile("" : "+v"(z));
+  u32x4_t z;  // made here, so that no zero vector stays live (or spilled) across the loops
+  asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
+               : "=v"(z[0]), "=v"(z[1]), "=v"(z[2]), "=v"(z[3]));
 #pragma unroll
   for (int i = 0; i < NB - 1; ++i)
     asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=&a"(o[i]) : "v"(z));
   // an empty segment reads the accumulators right away
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0\n\ts_nop 7\n\ts_nop 7" : "=&a"(o[NB - 1])
                : "v"(z));
+}
+// 16-byte global load that the compiler does not track: the caller waits for it with an
+// explicit vmcnt and reads the destination only after that wait.
+template <int OFF>
+__device__ __forceinline__ void gload16(u32x4_t& d, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2 ; qload" : "=v"(d) : "v"(p), "n"(OFF) : "memory");
+}
+// Lane index, recomputed where it is used: values derived from it (query and output
+// addresses) are then rebuilt at each segment instead of held in VGPRs across the tile
+// loop, where the register allocator would spill them; a spill reload is a vector-memory
+// load, and waiting for it would drain the DMA loads in flight.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 // Keeps an accumulator in AGPRs up to this point, so that the compiler copies it to
 // VGPRs only where it is read, one block at a time (not all 256 registers at once).
@@ -289,6 +305,18 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   const int row0 = hg * kGroupRows;
   const int RG = min(kGroupRows, R - row0);  // rows of this group
   const bool has_rows = 32 * w < RG;         // wave-uniform
+  // token t and head h of this lane's row 32w + l%32 of the group: the division is done
+  // once per wave on uniform values, the lane's remainder by at most 32 subtractions
+  // (no per-lane reciprocal held across the loops)
+  const int tw = (row0 + 32 * w) / a.N, hw = (row0 + 32 * w) - tw * a.N;
+  auto row_th = [&](int i, int& t, int& h) __attribute__((always_inline)) {
+    t = tw;
+    h = hw + i;
+    while (h >= a.N) {
+      h -= a.N;
+      ++t;
+    }
+  };
   const int32_t* segs = a.segs;
   const int s_beg = ld_uniform(a.part_begin + part), s_end = ld_uniform(a.part_begin + part + 1);
   const float c = a.qk_scale_log2;
@@ -382,8 +410,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   // row lane / 8, rope values 8 (lane % 8) .. +7.
   auto widen = [&](uint32_t raw, uint32_t dst, auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
-    const int row = i < 8 ? i : (lane >> 3);
-    const int col8 = i < 8 ? lane : 64 + (lane & 7);
+    const int ln = i < 8 ? lane : lane_now();  // (i = 8: no lane offset kept live for it)
+    const int row = i < 8 ? i : (ln >> 3);
+    const int col8 = i < 8 ? ln : 64 + (ln & 7);
     const u32x2_t v = *(const u32x2_t*)(smem + (raw - smem0) + row * kHead + 8 * col8);
     const u32x2_t lo = fp8x4_to_bf16x4(v[0]), hi = fp8x4_to_bf16x4(v[1]);
     *(u32x4_t*)(smem + dst + (8 * w + row) * kRowB + 16 * col8) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
@@ -397,6 +426,40 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   // receives those 4 keys of column +j): for k-step s the keys are x = h2 + 16s (e = 0..3)
   // and x + 2 (e = 4..7), matching the B operand P^T = elements 8s..8s+7 of S^T.
   const uint32_t vbase = (uint32_t)(h2 + 4 * ((lane & 15) >> 2)) * kRowB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
+  // ---- queries: the B operand of S^T = K . Q^T, 36 x 8 bf16 per lane (lane: row 32w +
+  // l%32 of the group, dims 16k + 8(l/32) .. +7 of k-step k).  Loaded ahead of use by
+  // untracked loads (the first segment's before the DMA prologue, each later one in the
+  // last step of the segment before) and waited for with a vmcnt that leaves the DMA
+  // loads issued after them in flight.  Padding rows load the wave's last row and are
+  // zeroed once loaded (zero queries give zero logits; their rows are never stored).
+  u32x4_t qr[36];
+  auto issue_q = [&](int b) __attribute__((always_inline)) {
+    const int ln = lane_now();
+    int t, h;
+    row_th(min(ln & 31, RG - 1 - 32 * w), t, h);
+    const int64_t tok = (int64_t)b * a.Sq + t;
+    const uint16_t* qn = a.q_nope + tok * a.q_nope_s_tok + (int64_t)h * a.q_nope_s_head + 8 * (ln >> 5);
+    const uint16_t* qp = a.q_pe + tok * a.q_pe_s_tok + (int64_t)h * a.q_pe_s_head + 8 * (ln >> 5);
+    static_for<32>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      gload16<32 * k>(qr[k], qn);
+    });
+    static_for<4>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      gload16<32 * k>(qr[32 + k], qp);
+    });
+  };
+  auto q_landed = [&]() __attribute__((always_inline)) {
+    if (32 * w + 32 > RG) {  // wave-uniform: the wave has padding rows
+      const bool pad = 32 * w + (lane_now() & 31) >= RG;
+#pragma unroll
+      for (int k = 0; k < 36; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qr[k][e] = pad ? 0u : qr[k][e];
+    }
+  };
+  if (has_rows && s_beg < s_end) issue_q(ld_uniform(segs + 4 * s_beg));
 
   Cursor pf = first_tile(segs, s_beg, s_end);  // next tile to load
   int issued = 0, done = 0;                    // tiles issued; tiles of finished segments
@@ -431,6 +494,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
       issued++;
     }
   }
+  if (has_rows && s_beg < s_end) {
+    // the first queries were issued before every DMA load
+    if constexpr (FP8) {
+      wait_vm<5>();
+    } else {
+      if (w0) wait_tiles<10>(issued);
+      else wait_tiles<9>(issued);
+    }
+    q_landed();
+  }
 
   for (int si = s_beg; si < s_end; ++si) {
     const Seg sg = load_seg(segs, si);
@@ -442,33 +515,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
     const int lim_lo = min(ke, L - a.Sq + 1);
     int lim = ke;
 
-    // Query rows of this wave: B operand of S^T = K . Q^T, 36 x 8 bf16 per lane
-    // (lane: row 32w + l%32, dims 16k + 8(l/32) .. +7 of k-step k).
-    u32x4_t qr[36];
     if (has_rows) {
-      const int rl = 32 * w + r32;
-      if (rl < RG) {
-        const int r = row0 + rl;
-        const int t = r / a.N, h = r - t * a.N;
-        const int64_t tok = (int64_t)b * a.Sq + t;
-        const uint16_t* qn = a.q_nope + tok * a.q_nope_s_tok + (int64_t)h * a.q_nope_s_head + 8 * h2;
-        const uint16_t* qp = a.q_pe + tok * a.q_pe_s_tok + (int64_t)h * a.q_pe_s_head + 8 * h2;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) qr[k] = *(const u32x4_t*)(qn + 16 * k);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) qr[32 + k] = *(const u32x4_t*)(qp + 16 * k);
-        lim = min(ke, L - (a.Sq - 1) + t);
-      } else {
-        // padding rows: zero queries give zero logits; their probabilities only reach
-        // output rows that are never stored
-#pragma unroll
-        for (int k = 0; k < 36; ++k) qr[k] = u32x4_t{0, 0, 0, 0};
-      }
-      // A wait the compiler sees: the query loads are complete before the tile loop,
-      // so it places no vmcnt waits there (those would also count the DMA loads in
-      // flight and drain the prefetch pipeline).  s_waitcnt vmcnt(0).
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      int t, h;
+      row_th(lane_now() & 31, t, h);
+      lim = min(ke, L - (a.Sq - 1) + t);
     }
+    const bool more = si + 1 < s_end;
+    bool dma_last = false;  // a DMA was issued in the last step (after the next queries)
 
     float m_ref = -INFINITY;  // reference maximum of this lane's row (log2 units)
     float nm = 0.f;           // exponent offset: -m_ref (0 while m_ref = -inf)
@@ -523,10 +576,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             raw_ready();
             static_for<9>([&](auto ic) __attribute__((always_inline)) { widen(raw_slot(g + 1), wst, ic); });
           }
+          if (more) issue_q(ld_uniform(segs + 4 * (si + 1)));
           if (do_dma) dma_raw(dt);
         } else {
+          if (more) issue_q(ld_uniform(segs + 4 * (si + 1)));
           if (do_dma) dma_all(dt);
         }
+        dma_last = do_dma;
       }
       if (has_rows) {
         // the DMA goes between the QK MFMAs unless the tile ends inside this wave's rows
@@ -581,9 +637,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
         // MFMA, at least one slot after the ops it reads. ----
         if (last || tq + kTile > lim_lo) {  // wave-uniform: some key of the tile is masked
           const int rem = last ? 0 : lim - tq;  // tile key k is visible iff k < rem
+          // element v holds key h2 + row_key(8(v/4) + v%4): compare with rem - h2 (the lane
+          // half recomputed here rather than 16 key indices held across the loop)
+          const int remh = rem - (lane_now() >> 5);
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            if (row_key(8 * (v >> 2) + 4 * h2 + (v & 3)) >= rem) sc[v] = -INFINITY;
+            if (row_key(8 * (v >> 2) + (v & 3)) >= remh) sc[v] = -INFINITY;
         }
         float mt[5], mf, mg, mx, ar[16], ex[16], tp[8], psum = 0.f;
         auto slot = [&](auto ic) __attribute__((always_inline)) {
@@ -700,25 +759,42 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
     }
     done = g0 + nt;
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");  // the last P.V MFMA's result is read next
+    // the next segment's queries (issued in the last step, or here after an empty segment)
+    if (has_rows && more) {
+      if (nt == 0) {
+        issue_q(ld_uniform(segs + 4 * (si + 1)));
+        wait_vm<0>();
+      } else if (!dma_last) {
+        wait_vm<0>();
+      } else if constexpr (FP8) {
+        wait_vm<5>();
+      } else {
+        if (w0) wait_vm<10>();
+        else wait_vm<9>();
+      }
+      q_landed();
+    }
 
     // ---- epilogue: o = O * kv_scale / l, lse = ln(sum exp) ----
     if (has_rows) {
       const float l_row = half_sum(l_acc);
-      const int rl = 32 * w + r32;
+      const int ln = lane_now(), hl = ln >> 5;
+      const int rl = 32 * w + (ln & 31);
       if (rl < RG) {
         const int r = row0 + rl;
         const float lse = (l_row > 0.f) ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
         const float f = (l_row > 0.f) ? a.out_scale / l_row : 0.f;
-        const int t = r / a.N, h = r - t * a.N;
+        int t, h;
+        row_th(ln & 31, t, h);
         if (pidx < 0) {
-          if (a.lse && h2 == 0) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
+          if (a.lse && hl == 0) a.lse[((int64_t)b * a.Sq + t) * a.N + h] = lse;
           uint16_t* orow = a.o + ((int64_t)b * a.Sq + t) * a.o_s_tok + (int64_t)h * a.o_s_head;
 #pragma unroll
           for (int cb = 0; cb < 16; ++cb) {
             acc_fence(O[cb]);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int col = 32 * cb + 8 * gq + 4 * h2;
+              const int col = 32 * cb + 8 * gq + 4 * hl;
               u32x2_t pk2;
               pk2[0] = pack_bf16x2(O[cb][4 * gq] * f, O[cb][4 * gq + 1] * f);
               pk2[1] = pack_bf16x2(O[cb][4 * gq + 2] * f, O[cb][4 * gq + 3] * f);
@@ -726,7 +802,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             }
           }
         } else {
-          if (h2 == 0) {
+          if (hl == 0) {
             a.ws_lse[(int64_t)pidx * R + r] = lse;
             a.ws_l[(int64_t)pidx * R + r] = l_row / a.out_scale;
           }
@@ -739,7 +815,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             acc_fence(O[cb]);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq)
-              *(f32x4_t*)(pblk + 4 * (64 * (4 * cb + gq) + lane)) =
+              *(f32x4_t*)(pblk + 4 * (64 * (4 * cb + gq) + ln)) =
                   f32x4_t{O[cb][4 * gq], O[cb][4 * gq + 1], O[cb][4 * gq + 2], O[cb][4 * gq + 3]};
           }
         }
