@@ -107,7 +107,8 @@ def algorithmic_work(w, seq_lens, with_lse):
 
 
 def cpu_baseline(inp, o_gpu, budget_s):
-    """The fp64 oracle, as it stands, on the first requests of the batch until budget_s."""
+    """The fp64 oracle, as it stands, on the requests of the batch in order (repeated passes)
+    until budget_s seconds of oracle time are used."""
     from oracle import attention as A
     from oracle.formats import bf16_to_f64
     w = inp.w
@@ -125,30 +126,36 @@ def cpu_baseline(inp, o_gpu, budget_s):
     qpe = bf16_to_f64(inp.q_pe)
     done, t_used = [], 0.0
     errs = []
-    for b in range(w.B):
-        sl = slice(b * w.Sq, (b + 1) * w.Sq)
-        t0 = time.perf_counter()
-        if w.absorb:
-            ql_b = A.absorb(q_nope[sl], W_UK)
-        else:
-            ql_b = ql[sl]
-        o, _ = A.latent_attention(ql_b, qpe[sl], inp.cache, w.kv_dtype, inp.kv_scale,
-                                  inp.block_table[b:b + 1], inp.seq_lens[b:b + 1], w.Sq, w.scale)
-        if w.absorb:
-            o = A.up_proj(o, W_UV)
-        t_used += time.perf_counter() - t0
-        done.append(b)
-        d = o_gpu[sl] - o
-        errs.append((float(np.max(np.abs(d))), float(np.sum(d * d)), float(np.sum(o * o))))
-        if t_used >= budget_s:
-            break
+    passes = 0
+    # whole passes over the batch (the first one also gives the parity sample) until the
+    # budget is used; a pass stops early only when the budget runs out inside it
+    while t_used < budget_s:
+        for b in range(w.B):
+            sl = slice(b * w.Sq, (b + 1) * w.Sq)
+            t0 = time.perf_counter()
+            if w.absorb:
+                ql_b = A.absorb(q_nope[sl], W_UK)
+            else:
+                ql_b = ql[sl]
+            o, _ = A.latent_attention(ql_b, qpe[sl], inp.cache, w.kv_dtype, inp.kv_scale,
+                                      inp.block_table[b:b + 1], inp.seq_lens[b:b + 1], w.Sq, w.scale)
+            if w.absorb:
+                o = A.up_proj(o, W_UV)
+            t_used += time.perf_counter() - t0
+            done.append(b)
+            if passes == 0:
+                d = o_gpu[sl] - o
+                errs.append((float(np.max(np.abs(d))), float(np.sum(d * d)), float(np.sum(o * o))))
+            if t_used >= budget_s:
+                break
+        passes += 1
     toks = len(done) * w.Sq
     max_abs = max(e[0] for e in errs)
     rel_l2 = float(np.sqrt(sum(e[1] for e in errs) / max(sum(e[2] for e in errs), 1e-300)))
     base = dict(value=toks / t_used, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"first {len(done)} of {w.B} requests ({toks} query tokens, "
-                       f"{int(inp.seq_lens[done].sum())} keys), {t_used:.1f} s of fp64 numpy")
-    return base, dict(requests=len(done), max_abs=max_abs, rel_l2=rel_l2)
+                sample=f"{len(done)} request calls over {passes} pass(es) of the {w.B}-request batch "
+                       f"({toks} query tokens, {int(inp.seq_lens[done].sum())} keys), {t_used:.1f} s of fp64 numpy")
+    return base, dict(requests=len(errs), max_abs=max_abs, rel_l2=rel_l2)
 
 
 def main():
