@@ -191,6 +191,26 @@ int merge_attn_states(void* out, float* out_lse, const void* prefix_o, const flo
                       const void* suffix_o, const float* suffix_lse, int32_t T, int32_t N,
                       int32_t D, int32_t o_dtype, void* stream);
 
+/*
+ * mla_concat_quant_q -- the decode query of an fp8 cache, concatenated and quantised
+ * with a static per-tensor scale (vLLM layers/attention/mla_attention, MLAAttention
+ * forward, decode branch: with an fp8 KV cache the absorbed query ql_nope and q_pe are
+ * concatenated and quantised to float8 with the layer's q_scale before the backend call).
+ *
+ *   q8[t, h, 0:512]   = e4m3fn(ql_nope[t, h, :] / q_scale)
+ *   q8[t, h, 512:576] = e4m3fn(q_pe[t, h, :] / q_scale)
+ * Each value: the bf16 input times the fp32 reciprocal of q_scale (rounded once),
+ * clamped to [-448, 448], rounded to the nearest OCP e4m3fn value, ties to even.
+ *
+ *   ql_nope [T, N, 512] bf16, q_pe [T, N, 64] bf16 (strides in elements, multiples of 8),
+ *   q8 [T, N, 576] e4m3fn bytes (strides in bytes, multiples of 16); all 16-byte aligned.
+ *   q_scale: finite and > 0.
+ * Errors: INVALID_ARG for null pointers, bad sizes, strides, alignment or q_scale.
+ */
+int mla_concat_quant_q(const void* ql_nope, int64_t ql_s_tok, int64_t ql_s_head, const void* q_pe,
+                       int64_t qpe_s_tok, int64_t qpe_s_head, float q_scale, void* q8, int64_t q8_s_tok,
+                       int64_t q8_s_head, int32_t T, int32_t N, void* stream);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* mla_last_error(void);
 

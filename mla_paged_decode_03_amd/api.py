@@ -50,6 +50,7 @@ _SIGS = {
     "mla_plan_compute_host": [_pi32, _i32, _i32, _i32, _i32, _pi32, _pi32, _pi32, _pi32, _pi32, _pi32],
     "mla_plan_export": [_vp, _pi32, _pi32, _pi32, _pi32],
     "mla_debug_gather_rows": [_vp, _vp, _i64, _vp, _vp],
+    "mla_concat_quant_q": [_vp, _i64, _i64, _vp, _i64, _i64, _f32, _vp, _i64, _i64, _i32, _i32, _vp],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -227,6 +228,22 @@ def merge_attn_states(out, out_lse, prefix_o, prefix_lse, suffix_o, suffix_lse, 
     _check(_lib.merge_attn_states(out.data_ptr(), _ptr(out_lse), prefix_o.data_ptr(),
                                   prefix_lse.data_ptr(), suffix_o.data_ptr(), suffix_lse.data_ptr(),
                                   T, N, D, dt, _stream(stream)))
+
+
+def mla_concat_quant_q(ql_nope, q_pe, q_scale: float, q8, stream=None):
+    """ql_nope [T,N,512] bf16, q_pe [T,N,64] bf16 -> q8 [T,N,576] float8_e4m3fn (or uint8)."""
+    _need(ql_nope, (torch.bfloat16,), "ql_nope")
+    _need(q_pe, (torch.bfloat16,), "q_pe")
+    _need(q8, (torch.float8_e4m3fn, torch.uint8), "q8")
+    T, N, _ = ql_nope.shape
+    if tuple(q_pe.shape) != (T, N, ROPE) or tuple(q8.shape) != (T, N, LKV + ROPE) or ql_nope.shape[2] != LKV:
+        raise ValueError("shapes must be ql_nope [T,N,512], q_pe [T,N,64], q8 [T,N,576]")
+    for t in (ql_nope, q_pe, q8):
+        if t.stride(2) != 1:
+            raise ValueError("the last dimension must be contiguous")
+    _check(_lib.mla_concat_quant_q(ql_nope.data_ptr(), ql_nope.stride(0), ql_nope.stride(1),
+                                   q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1), float(q_scale),
+                                   q8.data_ptr(), q8.stride(0), q8.stride(1), T, N, _stream(stream)))
 
 
 def mla_plan_compute_host(seq_lens, Sq: int, N: int, num_cus: int):

@@ -404,6 +404,35 @@ int merge_attn_states(void* out, float* out_lse, const void* prefix_o, const flo
   return e == hipSuccess ? MLA_OK : hip_fail(e, "merge launch");
 }
 
+int mla_concat_quant_q(const void* ql_nope, int64_t ql_s_tok, int64_t ql_s_head, const void* q_pe,
+                       int64_t qpe_s_tok, int64_t qpe_s_head, float q_scale, void* q8, int64_t q8_s_tok,
+                       int64_t q8_s_head, int32_t T, int32_t N, void* stream) {
+  if (!ql_nope || !q_pe || !q8) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (T < 0 || N < 1) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (!(q_scale > 0.f) || !std::isfinite(q_scale)) return fail(MLA_ERR_INVALID_ARG, "q_scale must be finite and > 0");
+  if (ql_s_head < mla::kLkv || ql_s_tok < (int64_t)N * ql_s_head || qpe_s_head < mla::kRope ||
+      qpe_s_tok < (int64_t)N * qpe_s_head || q8_s_head < mla::kHead || q8_s_tok < (int64_t)N * q8_s_head)
+    return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  if (!aligned(ql_nope, 16) || !aligned(q_pe, 16) || !aligned(q8, 16) || ql_s_tok % 8 || ql_s_head % 8 ||
+      qpe_s_tok % 8 || qpe_s_head % 8 || q8_s_tok % 16 || q8_s_head % 16)
+    return fail(MLA_ERR_INVALID_ARG, "rows must be 16-byte aligned (pointers and strides)");
+  mla::QuantArgs a{};
+  a.ql = (const uint16_t*)ql_nope;
+  a.ql_s_tok = ql_s_tok;
+  a.ql_s_head = ql_s_head;
+  a.qpe = (const uint16_t*)q_pe;
+  a.qpe_s_tok = qpe_s_tok;
+  a.qpe_s_head = qpe_s_head;
+  a.q8 = (uint8_t*)q8;
+  a.q8_s_tok = q8_s_tok;
+  a.q8_s_head = q8_s_head;
+  a.inv_scale = 1.0f / q_scale;
+  a.T = T;
+  a.N = N;
+  hipError_t e = mla::launch_concat_quant_q(a, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "quant launch");
+}
+
 int mla_debug_gather_rows(mla_plan plan, const int32_t* block_table, int64_t block_table_s_req,
                           int64_t* rows_out, void* stream) {
   if (!plan || !block_table || !rows_out) return fail(MLA_ERR_INVALID_ARG, "null pointer");

@@ -43,7 +43,19 @@ struct MergeArgs {
   int32_t Sq, N;
 };
 
+struct QuantArgs {
+  const uint16_t* ql;   // [T, N, 512] bf16
+  int64_t ql_s_tok, ql_s_head;
+  const uint16_t* qpe;  // [T, N, 64] bf16
+  int64_t qpe_s_tok, qpe_s_head;
+  uint8_t* q8;          // [T, N, 576] e4m3fn
+  int64_t q8_s_tok, q8_s_head;
+  float inv_scale;      // 1 / q_scale, rounded once to fp32
+  int32_t T, N;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_concat_quant_q(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_split_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(void* out, float* out_lse, const void* prefix_o, const float* prefix_lse,
                             const void* suffix_o, const float* suffix_lse, int64_t rows, int32_t D,

@@ -129,3 +129,23 @@ def test_gemm_and_merge_shape_errors():
     assert api._lib.merge_attn_states(p16, None, p16, p16, p16, p16, 1, 1, 16, 5, None) == \
         api.MLA_ERR_UNSUPPORTED
     assert api._lib.mla_absorb_q(p16 + 2, p16, p16, 1, 1, 128, 512, None) == api.MLA_ERR_INVALID_ARG
+
+
+def test_concat_quant_argument_errors():
+    buf = (C.c_uint8 * 4096)()
+    p16 = (C.cast(buf, C.c_void_p).value + 15) // 16 * 16
+    q = api._lib.mla_concat_quant_q
+    ok = dict(ql=p16, qls=512, qlh=512, qp=p16, qps=64, qph=64, s=1.0, q8=p16, q8s=576, q8h=576, T=1, N=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return q(a["ql"], a["qls"], a["qlh"], a["qp"], a["qps"], a["qph"], a["s"], a["q8"], a["q8s"],
+                 a["q8h"], a["T"], a["N"], None)
+    assert call(ql=None) == api.MLA_ERR_INVALID_ARG
+    assert call(q8=None) == api.MLA_ERR_INVALID_ARG
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(s=s) == api.MLA_ERR_INVALID_ARG and "q_scale" in api.mla_last_error()
+    assert call(q8h=570) == api.MLA_ERR_INVALID_ARG          # head stride below 576
+    assert call(q8h=584, q8s=584) == api.MLA_ERR_INVALID_ARG  # not a multiple of 16
+    assert call(ql=p16 + 2) == api.MLA_ERR_INVALID_ARG       # misaligned
+    assert call(N=0) == api.MLA_ERR_INVALID_ARG
