@@ -36,6 +36,7 @@ import numpy as np  # noqa: E402
 METRIC = "MLA decode tokens/s, HBM GB/s and MFMA TFLOP/s (% roofline), DSV3 shape"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 LKV, ROPE = 512, 64
 WANT_LSE = {"tiny": True, "dsv3": False, "longtail": False, "verify": False, "fp8": True}
 
@@ -106,7 +107,7 @@ def algorithmic_work(w, seq_lens, with_lse):
     return out
 
 
-def cpu_baseline(inp, o_gpu, budget_s):
+def cpu_baseline(inp, o_gpu, budget_s, q_scale=None):
     """The fp64 oracle, as it stands, on the requests of the batch in order (repeated passes)
     until budget_s seconds of oracle time are used."""
     from oracle import attention as A
@@ -124,6 +125,13 @@ def cpu_baseline(inp, o_gpu, budget_s):
     else:
         ql = bf16_to_f64(inp.q)
     qpe = bf16_to_f64(inp.q_pe)
+    if q_scale is not None:
+        # fp8 queries: the oracle is fed the same quantised query (outside the timed part)
+        from oracle import quant as Q
+        from oracle.formats import E4M3FN_TABLE
+        q8 = Q.concat_quant_q(inp.q, inp.q_pe, q_scale)
+        ql = E4M3FN_TABLE[q8[..., :LKV]] * q_scale
+        qpe = E4M3FN_TABLE[q8[..., LKV:]] * q_scale
     done, t_used = [], 0.0
     errs = []
     passes = 0
@@ -168,6 +176,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--q8", action="store_true",
+                    help="fp8 cache only: quantise the query to fp8 (static per-tensor scale) and "
+                         "run the fp8-query decode")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (no collectives); "
@@ -183,6 +194,9 @@ def main():
     from mla_paged_decode_03_amd import inputs as gen
 
     w = gen.workload(args.workload)
+    if args.q8 and w.kv_dtype != "fp8":
+        print("--q8 needs a workload with an fp8 cache", file=sys.stderr)
+        sys.exit(2)
     t_gen = time.perf_counter()
     inp = gen.generate(w)
     t_gen = time.perf_counter() - t_gen
@@ -212,6 +226,14 @@ def main():
         o_up = torch.empty((T, N, w.V), dtype=torch.bfloat16, device=dev)
     else:
         ql = bf16(inp.q)
+    q_scale, q8 = None, None
+    if args.q8:
+        # static per-tensor query scale, calibrated once from the data: max |q| / 448
+        def f32(bits):
+            return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        amax = max(float(np.abs(f32(inp.q)).max()), float(np.abs(f32(inp.q_pe)).max()))
+        q_scale = float(np.float32(amax / 448.0))
+        q8 = torch.empty((T, N, LKV + ROPE), dtype=torch.uint8, device=dev)
 
     t0 = time.perf_counter()
     plan = api.mla_decode_plan(inp.seq_lens, w.Sq, N, w.page_size, inp.block_table.shape[1], dt)
@@ -219,12 +241,20 @@ def main():
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
     work, red = api.mla_plan_export(plan)
 
+    def attend():
+        if args.q8:
+            api.mla_decode_attend_q8(plan, q8, q_scale, cache, bt, sl, w.scale, inp.kv_scale, o_lat, lse, ws)
+        else:
+            api.mla_decode_attend(plan, ql, q_pe, cache, bt, sl, w.scale, inp.kv_scale, o_lat, lse, ws)
+
     def step(ev=None):
         if w.absorb:
             api.mla_absorb_q(q_nope, W_UK, ql)
+        if args.q8:
+            api.mla_concat_quant_q(ql, q_pe, q_scale, q8)
         if ev is not None:
             ev[0].record()
-        api.mla_decode_attend(plan, ql, q_pe, cache, bt, sl, w.scale, inp.kv_scale, o_lat, lse, ws)
+        attend()
         if ev is not None:
             ev[1].record()
         api.mla_decode_reduce(plan, o_lat, lse, ws)
@@ -263,8 +293,7 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K * 1e3
-    dec_us = timed(lambda: api.mla_decode_attend(plan, ql, q_pe, cache, bt, sl, w.scale, inp.kv_scale,
-                                                 o_lat, lse, ws))
+    dec_us = timed(attend)
     red_us = timed(lambda: api.mla_decode_reduce(plan, o_lat, lse, ws))
     step_dec_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
 
@@ -283,34 +312,41 @@ def main():
     work_alg = algorithmic_work(w, inp.seq_lens, with_lse)
     hbm_gbs = work_alg["bytes"] / (dec_us * 1e-6) / 1e9
     tflops = work_alg["flops"] / (dec_us * 1e-6) / 1e12
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    # MFMA peak: bf16 for both contractions, or with fp8 queries fp8 for QK (576 of the 1088
+    # flops per key and row) and bf16 for P.V: the blend is the harmonic mean by flops
+    mfma_peak = BF16_PEAK_TFLOPS
+    if args.q8:
+        fq = (LKV + ROPE) / (LKV + ROPE + LKV)
+        mfma_peak = 1.0 / (fq / FP8_PEAK_TFLOPS + (1 - fq) / BF16_PEAK_TFLOPS)
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "hbm" if work_alg["flops"] / work_alg["bytes"] < ridge else "mfma"
     traffic = load_traffic(w.name)
     if bound == "hbm":
         roof = dict(bound="hbm", achieved=round(hbm_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(hbm_gbs / HBM_PEAK_GBS, 4), traffic=traffic)
     else:
-        roof = dict(bound="mfma", achieved=round(tflops, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tflops / BF16_PEAK_TFLOPS, 4), traffic=traffic)
-    t_roof_us = max(work_alg["bytes"] / (HBM_PEAK_GBS * 1e9), work_alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+        roof = dict(bound="mfma", achieved=round(tflops, 1), peak=round(mfma_peak, 1), unit="TFLOP/s",
+                    frac=round(tflops / mfma_peak, 4), traffic=traffic)
+    t_roof_us = max(work_alg["bytes"] / (HBM_PEAK_GBS * 1e9), work_alg["flops"] / (mfma_peak * 1e12)) * 1e6
 
     tokens_per_s = T / (ms_per_step * 1e-3)
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-kv/bf16-mfma", "data": "synthetic",
+        "dtype": "bf16" if w.kv_dtype == "bf16" else ("fp8-kv/fp8-qk/bf16-pv" if args.q8 else "fp8-kv/bf16-mfma"),
+        "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Sq": w.Sq, "N": N, "Lkv": LKV, "R": ROPE,
                    "page_size": w.page_size, "kv_dtype": w.kv_dtype,
                    "seq_lens": f"{w.seqlen_kind}[{w.seqlen_lo},{w.seqlen_hi}] seed {w.seed}",
                    "sum_keys": int(inp.seq_lens.sum()), "absorb_up": bool(w.absorb),
-                   "lse": with_lse},
+                   "lse": with_lse, "q8": bool(args.q8), "q_scale": q_scale},
         "roofline": roof,
         "decode_kernel_us": round(dec_us, 2), "reduce_kernel_us": round(red_us, 2),
         "decode_in_step_us": round(step_dec_us, 2),
         "decode_kernel_cold_us": None if cold_us is None else round(cold_us, 2),
         "hbm_gbps": round(hbm_gbs, 1), "tflops": round(tflops, 1),
-        "frac_hbm": round(hbm_gbs / HBM_PEAK_GBS, 4), "frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "frac_hbm": round(hbm_gbs / HBM_PEAK_GBS, 4), "frac_mfma": round(tflops / mfma_peak, 4),
         "frac_roofline": round(t_roof_us / dec_us, 4),
         "algorithmic": work_alg, "plan_host_us": round(plan_us, 1),
         "plan": {"parts": int(work[:, 0].max()) + 1 if len(work) else 0, "segments": int(len(work)),
@@ -322,7 +358,7 @@ def main():
         torch.cuda.synchronize()
         o_dev = o_up if w.absorb else o_lat
         o_np = o_dev.float().cpu().numpy().astype(np.float64)
-        base, parity = cpu_baseline(inp, o_np, args.cpu_budget)
+        base, parity = cpu_baseline(inp, o_np, args.cpu_budget, q_scale)
         line["cpu_baseline"] = base
         line["parity_sample"] = parity
     plan.destroy()

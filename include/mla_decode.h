@@ -152,6 +152,37 @@ int mla_decode_reduce(mla_plan plan, void* o_latent, int64_t o_s_tok, int64_t o_
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_run_q8 / mla_decode_attend_q8 -- mla_decode_run / mla_decode_attend for
+ * an fp8 cache with an fp8 query: q8 = [ql_nope | q_pe] quantised with the static
+ * per-tensor q_scale (mla_concat_quant_q; vLLM MLAAttention quantises the decode query
+ * whenever the cache is fp8 and the backend takes a quantised query, and the ROCm
+ * backend then runs with an fp8 query, rocm_aiter_mla page).  The logits are
+ *   s_j = scale * q_scale * kv_scale * (q8[t,h] . cache[row_j])
+ * in fp32 from exact fp8 products (the softmax scale takes q_scale together with the
+ * cache scale, as the flashinfer page's bmm1_scale does); everything after the logits
+ * is as in mla_decode_run (values widened to bf16, bf16 P.V, fp32 accumulation).
+ *
+ *  q8        [B*Sq, N, 576] float8 e4m3fn bytes; strides q8_s_tok, q8_s_head in bytes,
+ *            multiples of 16, q8_s_head >= 576; 16-byte aligned.
+ *  q_scale   finite and > 0.
+ *  The plan must be for an fp8 cache (MLA_ERR_UNSUPPORTED otherwise).  All other
+ *  arguments, ownership and errors as mla_decode_run; mla_decode_reduce completes
+ *  attend_q8 as it completes attend.
+ */
+int mla_decode_run_q8(mla_plan plan, const void* q8, int64_t q8_s_tok, int64_t q8_s_head, float q_scale,
+                      const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
+                      int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
+                      int64_t block_table_s_req, const int32_t* seq_lens, float scale, float kv_scale,
+                      void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+int mla_decode_attend_q8(mla_plan plan, const void* q8, int64_t q8_s_tok, int64_t q8_s_head, float q_scale,
+                         const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
+                         int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
+                         int64_t block_table_s_req, const int32_t* seq_lens, float scale, float kv_scale,
+                         void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * mla_absorb_q -- ql_nope[t,h,l] = sum_p q_nope[t,h,p] * W_UK[l,h,p].
  * mla/common.py docstring, "Data-Movement Friendly Approach" (einsum
  * "snh,lnh->snl"); the layer runs it as a per-head bmm (N,B,P)x(N,P,L)

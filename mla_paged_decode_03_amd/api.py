@@ -51,6 +51,10 @@ _SIGS = {
     "mla_plan_export": [_vp, _pi32, _pi32, _pi32, _pi32],
     "mla_debug_gather_rows": [_vp, _vp, _i64, _vp, _vp],
     "mla_concat_quant_q": [_vp, _i64, _i64, _vp, _i64, _i64, _f32, _vp, _i64, _i64, _i32, _i32, _vp],
+    "mla_decode_run_q8": [_vp, _vp, _i64, _i64, _f32, _vp, _vp, _i64, _i64, _i32, _vp, _i64, _vp, _f32, _f32,
+                          _vp, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mla_decode_attend_q8": [_vp, _vp, _i64, _i64, _f32, _vp, _vp, _i64, _i64, _i32, _vp, _i64, _vp, _f32,
+                             _f32, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -182,6 +186,33 @@ def mla_decode_attend(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, sc
     _check(_lib.mla_decode_attend(*_decode_args(plan, q_nope, q_pe, cache, block_table, seq_lens,
                                                 scale, kv_scale, o_latent, lse, workspace, stream,
                                                 cache_k_pe)))
+
+
+def _decode_args_q8(plan: Plan, q8, q_scale, cache, block_table, seq_lens, scale, kv_scale,
+                    o_latent, lse, workspace, stream, cache_k_pe):
+    _need(q8, (torch.float8_e4m3fn, torch.uint8), "q8")
+    if q8.stride(2) != 1:
+        raise ValueError("the last dimension of q8 must be contiguous")
+    # the bf16 argument checks, with the fp8 query standing in for q_nope / q_pe
+    args = list(_decode_args(plan, o_latent, o_latent, cache, block_table, seq_lens, scale, kv_scale,
+                             o_latent, lse, workspace, stream, cache_k_pe))
+    return (args[0], q8.data_ptr(), q8.stride(0), q8.stride(1), float(q_scale)) + tuple(args[7:])
+
+
+def mla_decode_run_q8(plan: Plan, q8, q_scale: float, cache, block_table, seq_lens, scale: float,
+                      kv_scale: float, o_latent, lse=None, workspace=None, stream=None, cache_k_pe=None):
+    """q8 [T,N,576] float8_e4m3fn ([ql_nope | q_pe] quantised with q_scale, see
+    mla_concat_quant_q); the cache must be fp8.  Other arguments as mla_decode_run."""
+    _check(_lib.mla_decode_run_q8(*_decode_args_q8(plan, q8, q_scale, cache, block_table, seq_lens, scale,
+                                                   kv_scale, o_latent, lse, workspace, stream, cache_k_pe)))
+
+
+def mla_decode_attend_q8(plan: Plan, q8, q_scale: float, cache, block_table, seq_lens, scale: float,
+                         kv_scale: float, o_latent, lse=None, workspace=None, stream=None, cache_k_pe=None):
+    """First phase of mla_decode_run_q8; same arguments."""
+    _check(_lib.mla_decode_attend_q8(*_decode_args_q8(plan, q8, q_scale, cache, block_table, seq_lens,
+                                                      scale, kv_scale, o_latent, lse, workspace, stream,
+                                                      cache_k_pe)))
 
 
 def mla_decode_reduce(plan: Plan, o_latent, lse=None, workspace=None, stream=None):

@@ -202,31 +202,48 @@ int mla_plan_export(mla_plan plan, int32_t* work_host, int32_t* n_items, int32_t
   return MLA_OK;
 }
 
-int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
-                   const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head,
-                   const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
-                   int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
-                   int64_t block_table_s_req, const int32_t* seq_lens, float scale,
-                   float kv_scale, void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+// Queries of one attend call: bf16 q_nope / q_pe, or (q8 != null) fp8 [ql_nope | q_pe]
+// with its static scale.
+struct Queries {
+  const void* q_nope = nullptr;
+  int64_t q_nope_s_tok = 0, q_nope_s_head = 0;
+  const void* q_pe = nullptr;
+  int64_t q_pe_s_tok = 0, q_pe_s_head = 0;
+  const void* q8 = nullptr;
+  int64_t q8_s_tok = 0, q8_s_head = 0;
+  float q_scale = 1.f;
+};
+
+static int attend(mla_plan plan, const Queries& q, const void* cache_kv_c, const void* cache_k_pe,
+                  int64_t cache_s_page, int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
+                  int64_t block_table_s_req, const int32_t* seq_lens, float scale, float kv_scale,
+                  void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   if (!plan) return fail(MLA_ERR_INVALID_ARG, "null plan");
-  if (!q_nope || !q_pe || !cache_kv_c || !cache_k_pe || !block_table || !seq_lens || !o_latent)
+  const bool qf8 = q.q8 != nullptr;
+  const bool fp8 = plan->kv_dtype == MLA_DT_FP8_E4M3FN;
+  if ((!qf8 && (!q.q_nope || !q.q_pe)) || !cache_kv_c || !cache_k_pe || !block_table || !seq_lens || !o_latent)
     return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (qf8 && !fp8) return fail(MLA_ERR_UNSUPPORTED, "fp8 queries need a plan for an fp8 cache");
   const auto& hp = plan->host;
-  if (q_nope_s_tok < 1 || q_nope_s_head < 1 || q_pe_s_tok < 1 || q_pe_s_head < 1 || o_s_tok < 1 ||
-      o_s_head < 1 || cache_s_page < 1 || cache_s_tok < 1 || block_table_s_req < plan->max_pages)
+  if ((!qf8 && (q.q_nope_s_tok < 1 || q.q_nope_s_head < 1 || q.q_pe_s_tok < 1 || q.q_pe_s_head < 1)) ||
+      (qf8 && (q.q8_s_head < mla::kHead || q.q8_s_tok < 1)) || o_s_tok < 1 || o_s_head < 1 ||
+      cache_s_page < 1 || cache_s_tok < 1 || block_table_s_req < plan->max_pages)
     return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  if (qf8 && (!std::isfinite(q.q_scale) || q.q_scale <= 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "q_scale must be finite and > 0");
   if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
   if (!std::isfinite(scale) || !std::isfinite(kv_scale) || scale <= 0.f || kv_scale <= 0.f)
     return fail(MLA_ERR_INVALID_ARG, "scale and kv_scale must be finite and > 0");
   // 16-byte loads of the queries and of cache pieces (8 bf16 or 16 fp8 values), 8-byte
   // output stores; the kernel forms the byte offset of a key within a 32-key tile in 32 bits.
-  const bool fp8 = plan->kv_dtype == MLA_DT_FP8_E4M3FN;
   const size_t cal = 16;
   if (cache_s_tok > (int64_t(1) << 24)) return fail(MLA_ERR_INVALID_ARG, "cache_s_tok too large");
-  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || q_nope_s_tok % 8 || q_nope_s_head % 8 ||
-      q_pe_s_tok % 8 || q_pe_s_head % 8)
+  if (!qf8 && (!aligned(q.q_nope, 16) || !aligned(q.q_pe, 16) || q.q_nope_s_tok % 8 || q.q_nope_s_head % 8 ||
+               q.q_pe_s_tok % 8 || q.q_pe_s_head % 8))
     return fail(MLA_ERR_INVALID_ARG, "queries need 16-byte aligned rows (pointer and strides)");
+  if (qf8 && (!aligned(q.q8, 16) || q.q8_s_tok % 16 || q.q8_s_head % 16))
+    return fail(MLA_ERR_INVALID_ARG, "fp8 queries need 16-byte aligned rows (pointer and strides)");
   const int64_t cel = fp8 ? 16 : 8;  // elements per 16 bytes
   if (!aligned(cache_kv_c, cal) || !aligned(cache_k_pe, cal) || cache_s_page % cel || cache_s_tok % cel)
     return fail(MLA_ERR_INVALID_ARG, "cache rows must be 16-byte aligned (pointers and strides)");
@@ -242,12 +259,15 @@ int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, i
   if (dev != plan->device) return fail(MLA_ERR_INVALID_ARG, "plan was made for another device");
 
   mla::DecodeArgs a{};
-  a.q_nope = (const uint16_t*)q_nope;
-  a.q_nope_s_tok = q_nope_s_tok;
-  a.q_nope_s_head = q_nope_s_head;
-  a.q_pe = (const uint16_t*)q_pe;
-  a.q_pe_s_tok = q_pe_s_tok;
-  a.q_pe_s_head = q_pe_s_head;
+  a.q_nope = (const uint16_t*)q.q_nope;
+  a.q_nope_s_tok = q.q_nope_s_tok;
+  a.q_nope_s_head = q.q_nope_s_head;
+  a.q_pe = (const uint16_t*)q.q_pe;
+  a.q_pe_s_tok = q.q_pe_s_tok;
+  a.q_pe_s_head = q.q_pe_s_head;
+  a.q8 = (const uint8_t*)q.q8;
+  a.q8_s_tok = q.q8_s_tok;
+  a.q8_s_head = q.q8_s_head;
   a.kv_c = cache_kv_c;
   a.k_pe = cache_k_pe;
   a.s_page = cache_s_page;
@@ -267,7 +287,7 @@ int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, i
                                                          mla::kLkv * 4)
                        : nullptr;
   a.ws_l = workspace ? a.ws_lse + (size_t)hp.num_partials * R : nullptr;
-  a.qk_scale_log2 = scale * kv_scale * 1.4426950408889634f;
+  a.qk_scale_log2 = scale * kv_scale * (qf8 ? q.q_scale : 1.f) * 1.4426950408889634f;
   a.out_scale = kv_scale;
   a.Sq = hp.Sq;
   a.N = hp.N;
@@ -275,9 +295,45 @@ int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, i
   a.num_parts = hp.num_parts;
   a.head_groups = hp.head_groups;
   hipStream_t s = (hipStream_t)stream;
-  e = mla::launch_decode(a, fp8, s);
+  e = mla::launch_decode(a, fp8, qf8, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return MLA_OK;
+}
+
+int mla_decode_attend(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
+                      const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head,
+                      const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
+                      int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
+                      int64_t block_table_s_req, const int32_t* seq_lens, float scale,
+                      float kv_scale, void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  Queries q;
+  q.q_nope = q_nope;
+  q.q_nope_s_tok = q_nope_s_tok;
+  q.q_nope_s_head = q_nope_s_head;
+  q.q_pe = q_pe;
+  q.q_pe_s_tok = q_pe_s_tok;
+  q.q_pe_s_head = q_pe_s_head;
+  return attend(plan, q, cache_kv_c, cache_k_pe, cache_s_page, cache_s_tok, num_pages, block_table,
+                block_table_s_req, seq_lens, scale, kv_scale, o_latent, o_s_tok, o_s_head, lse, workspace,
+                workspace_bytes, stream);
+}
+
+int mla_decode_attend_q8(mla_plan plan, const void* q8, int64_t q8_s_tok, int64_t q8_s_head, float q_scale,
+                         const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page,
+                         int64_t cache_s_tok, int32_t num_pages, const int32_t* block_table,
+                         int64_t block_table_s_req, const int32_t* seq_lens, float scale, float kv_scale,
+                         void* o_latent, int64_t o_s_tok, int64_t o_s_head, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!q8) return fail(MLA_ERR_INVALID_ARG, "null tensor pointer");
+  Queries q;
+  q.q8 = q8;
+  q.q8_s_tok = q8_s_tok;
+  q.q8_s_head = q8_s_head;
+  q.q_scale = q_scale;
+  return attend(plan, q, cache_kv_c, cache_k_pe, cache_s_page, cache_s_tok, num_pages, block_table,
+                block_table_s_req, seq_lens, scale, kv_scale, o_latent, o_s_tok, o_s_head, lse, workspace,
+                workspace_bytes, stream);
 }
 
 static int check_workspace(mla_plan plan, void* workspace, size_t workspace_bytes) {
@@ -331,6 +387,19 @@ int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int6
                              cache_kv_c, cache_k_pe, cache_s_page, cache_s_tok, num_pages, block_table,
                              block_table_s_req, seq_lens, scale, kv_scale, o_latent, o_s_tok, o_s_head,
                              lse, workspace, workspace_bytes, stream);
+  if (rc) return rc;
+  if (plan->host.reduce.empty()) return MLA_OK;
+  return mla_decode_reduce(plan, o_latent, o_s_tok, o_s_head, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_run_q8(mla_plan plan, const void* q8, int64_t q8_s_tok, int64_t q8_s_head, float q_scale,
+                      const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page, int64_t cache_s_tok,
+                      int32_t num_pages, const int32_t* block_table, int64_t block_table_s_req,
+                      const int32_t* seq_lens, float scale, float kv_scale, void* o_latent, int64_t o_s_tok,
+                      int64_t o_s_head, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = mla_decode_attend_q8(plan, q8, q8_s_tok, q8_s_head, q_scale, cache_kv_c, cache_k_pe, cache_s_page,
+                                cache_s_tok, num_pages, block_table, block_table_s_req, seq_lens, scale, kv_scale,
+                                o_latent, o_s_tok, o_s_head, lse, workspace, workspace_bytes, stream);
   if (rc) return rc;
   if (plan->host.reduce.empty()) return MLA_OK;
   return mla_decode_reduce(plan, o_latent, o_s_tok, o_s_head, lse, workspace, workspace_bytes, stream);

@@ -40,7 +40,18 @@ static_assert(kDmaN == 37, "the last DMA instruction of a tile is the only parti
 constexpr int kSmemBytes = kStages * kStageB;  // 149504
 constexpr float kRescaleAt = 8.f;  // log2 units a tile maximum may exceed the reference by
 
-__shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+// fp8 queries (fp8 cache only): raw e4m3 tiles, read as they are by the fp8 QK, in a
+// 4-slot ring; the value columns of each tile are widened into one of two bf16 stages
+// (the stage layout above, rope columns unused) for the bf16 P.V.
+constexpr int kQRowB = 592;                    // raw row: 576 bytes + 16 pad
+constexpr int kQRowC = kQRowB / 16;            // 37 chunks (odd: conflict-free reads)
+constexpr int kQSlotB = kTile * kQRowB;        // 18944
+constexpr int kQSlots = 4;
+constexpr int kQVBase = kQSlots * kQSlotB;     // 75776: the two value stages follow
+constexpr int kQSmem = kQVBase + 2 * kStageB;  // 150528
+constexpr int kSmemAll = kQSmem > kSmemBytes ? kQSmem : kSmemBytes;
+
+__shared__ __attribute__((aligned(1024))) char smem[kSmemAll];
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -246,6 +257,25 @@ __device__ __forceinline__ void mfma_a_nw(f32x16_t& d, const u32x4_t& a, const u
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 
+// fp8 x fp8 MFMA (v_mfma_f32_32x32x64_f8f6f4, both operands e4m3, 16 passes): D += A B
+// over 64 k.  Lane l holds A[l%32][k] and B[k][l%32] for 32 values of k in the lane
+// half l/32; which 32 is the same for A and B, so a contraction only needs both operands
+// loaded alike.  The last of a chain pads the 18 wait states a VALU read of D needs.
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ u32x8_t cat8(const u32x4_t& lo, const u32x4_t& hi) {
+  return u32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ void mfma8_first(f32x16_t& d, const u32x8_t& a, const u32x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma8_acc(f32x16_t& d, const u32x8_t& a, const u32x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma8_last(f32x16_t& d, const u32x8_t& a, const u32x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d)
+               : "v"(a), "v"(b));
+}
+
 // HBM -> LDS, 16 bytes per lane at lds_base + IMM + 16 lane, from gbase + voff.
 template <int IMM>
 __device__ __forceinline__ void dma16_si(const void* gbase, uint32_t voff, uint32_t lds_base) {
@@ -285,8 +315,12 @@ static_assert(kRawBase + 4 * 2 * kRawWaveTile <= kSmemBytes, "fp8 stages fit");
 // FAST: pages of a multiple of 32 keys (a tile sits in one page) and the rope columns
 // right after the latent ones in each cache row (one base for the whole row).
 // FP8: e4m3 cache, widened to bf16 in LDS (every e4m3 value is exact in bf16).
-template <bool FAST, bool FP8>
+// QF8 (with FP8): e4m3 queries; QK on the fp8 MFMA over the raw tile, only the value
+// columns widened to bf16 for P.V.
+template <bool FAST, bool FP8, bool QF8>
 __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
+  static_assert(!QF8 || FP8, "fp8 queries go with an fp8 cache");
+  constexpr bool RAWW = FP8 && !QF8;  // fp8 cache widened whole, per-wave raw ring
   // K fragment ring depth, and DMA steps issued before the first QK MFMA (they fill the
   // wait for the first fragments); chosen by measurement on the DSV3 and verify shapes
   constexpr int KRING = 6, DMA0 = 2;
@@ -418,6 +452,71 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
     *(u32x4_t*)(smem + dst + (8 * w + row) * kRowB + 16 * col8) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   };
 
+  // ---- fp8 queries: all waves load each raw tile into its slot of the 4-slot ring: wave
+  // w issues instructions j = w + 4n (n = 0..4, j < 19; j = 18: lanes 0..31).  Lane l of
+  // instruction j writes slot chunk p = 64j + l = row p / 37, chunk p % 37 (the pad, chunk
+  // 36, takes a copy of chunk 35).  A tile is PERQ = 5 (wave 3: 4) instructions per wave.
+  auto q8_row = [&](int n) __attribute__((always_inline)) { return (64 * (w + 4 * n) + lane) / kQRowC; };
+  auto q8_col = [&](int n) __attribute__((always_inline)) {
+    return min((64 * (w + 4 * n) + lane) % kQRowC, kQRowC - 2);
+  };
+  uint32_t qvo[5];  // FAST: byte offsets from the tile's first row
+  if constexpr (QF8) {
+#pragma unroll
+    for (int n = 0; n < 5; ++n) qvo[n] = (uint32_t)q8_row(n) * st + 16u * (uint32_t)q8_col(n);
+  }
+  const int qwkey = (64 * (w + 16) + 63) / kQRowC;  // upper bound of the rows this wave loads
+  auto dma_q8_one = [&](const DmaTile& t, auto nc) __attribute__((always_inline)) {
+    constexpr int n = decltype(nc)::value;
+    if constexpr (n == 4) {
+      if (w == 3) return;                // j = 19: past the tile (wave-uniform)
+      if (w == 2 && lane >= 32) return;  // j = 18: the tile's last 32 chunks
+    }
+    if constexpr (FAST) {
+      dma16_si<4096 * n>(t.kv, qvo[n], __builtin_amdgcn_readfirstlane(t.lds + 1024 * w));
+    } else {
+      // generic pages: the rows of this instruction (at most three) through the block table
+      const int k0 = (64 * (w + 4 * n)) / kQRowC;  // wave-uniform
+      const int64_t rb0 = row_bytes(a, t.bt_row, t.ts + min(k0, t.kmax), 1);
+      const int64_t rb1 = row_bytes(a, t.bt_row, t.ts + min(k0 + 1, t.kmax), 1);
+      const int64_t rb2 = row_bytes(a, t.bt_row, t.ts + min(k0 + 2, t.kmax), 1);
+      const int kr = q8_row(n) - k0, col = q8_col(n);
+      const int64_t rb = kr == 0 ? rb0 : (kr == 1 ? rb1 : rb2);
+      const char* src = col < 32 ? (const char*)t.kv + rb + 16 * col : (const char*)t.pe + rb + 16 * (col - 32);
+      dma16(src, t.lds + 1024 * (w + 4 * n));
+    }
+  };
+  auto dma_q8 = [&](const DmaTile& t) __attribute__((always_inline)) {
+    // rows past the tile's last key load that key (FAST: offsets moved there and back)
+    const bool clamp = FAST && t.kmax < qwkey;
+    if (clamp) {
+#pragma unroll
+      for (int n = 0; n < 5; ++n) qvo[n] -= (uint32_t)max(q8_row(n) - t.kmax, 0) * st;
+    }
+    static_for<5>([&](auto nc) __attribute__((always_inline)) { dma_q8_one(t, nc); });
+    if (clamp) {
+#pragma unroll
+      for (int n = 0; n < 5; ++n) qvo[n] += (uint32_t)max(q8_row(n) - t.kmax, 0) * st;
+    }
+  };
+  // Value columns of this wave's rows 8w..8w+7 of a raw tile, widened into a bf16 value
+  // stage: lane l takes row 8w + l%8, bytes 64(l/8) .. +63 (four 16-byte reads, eight
+  // 16-byte writes; part i = 0..3 converts read i).
+  const uint32_t q8wsrc = (uint32_t)(8 * w + (lane & 7)) * kQRowB + 64 * (lane >> 3);
+  const uint32_t q8wdst = (uint32_t)(8 * w + (lane & 7)) * kRowB + 128 * (lane >> 3);
+  auto widen8_read = [&](uint32_t slot, u32x4_t (&wr)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[i] = *(const u32x4_t*)(smem + slot + q8wsrc + 16 * i);
+  };
+  auto widen8_part = [&](uint32_t vstage, const u32x4_t (&wr)[4], int i) __attribute__((always_inline)) {
+    const u32x2_t b0 = fp8x4_to_bf16x4(wr[i][0]), b1 = fp8x4_to_bf16x4(wr[i][1]);
+    const u32x2_t b2 = fp8x4_to_bf16x4(wr[i][2]), b3 = fp8x4_to_bf16x4(wr[i][3]);
+    *(u32x4_t*)(smem + vstage + q8wdst + 32 * i) = u32x4_t{b0[0], b0[1], b1[0], b1[1]};
+    *(u32x4_t*)(smem + vstage + q8wdst + 32 * i + 16) = u32x4_t{b2[0], b2[1], b3[0], b3[1]};
+  };
+  // fp8 QK A operand: key row_key(r32) of the raw tile, 32 bytes of k-step c at +64c
+  const uint32_t kq8base = (uint32_t)row_key(r32) * kQRowB + 32 * h2;
+
   // ---- LDS read addresses (bytes from a stage base) ----
   // QK A operand: key row_key(r32), logical chunk 2k + h2 at kbase + 32 k.
   const uint32_t kbase = (uint32_t)row_key(r32) * kRowB + 16 * h2;
@@ -433,28 +532,39 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   // last step of the segment before) and waited for with a vmcnt that leaves the DMA
   // loads issued after them in flight.  Padding rows load the wave's last row and are
   // zeroed once loaded (zero queries give zero logits; their rows are never stored).
-  u32x4_t qr[36];
+  // fp8 queries: 9 k-steps of 64 dims, 32 bytes per lane (dims 64c + 32(l/32) .. +31)
+  // in qr[2c], qr[2c + 1].
+  constexpr int NQ = QF8 ? 18 : 36;
+  u32x4_t qr[NQ];
   auto issue_q = [&](int b) __attribute__((always_inline)) {
     const int ln = lane_now();
     int t, h;
     row_th(min(ln & 31, RG - 1 - 32 * w), t, h);
     const int64_t tok = (int64_t)b * a.Sq + t;
-    const uint16_t* qn = a.q_nope + tok * a.q_nope_s_tok + (int64_t)h * a.q_nope_s_head + 8 * (ln >> 5);
-    const uint16_t* qp = a.q_pe + tok * a.q_pe_s_tok + (int64_t)h * a.q_pe_s_head + 8 * (ln >> 5);
-    static_for<32>([&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value;
-      gload16<32 * k>(qr[k], qn);
-    });
-    static_for<4>([&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value;
-      gload16<32 * k>(qr[32 + k], qp);
-    });
+    if constexpr (QF8) {
+      const uint8_t* q8 = a.q8 + tok * a.q8_s_tok + (int64_t)h * a.q8_s_head + 32 * (ln >> 5);
+      static_for<18>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        gload16<64 * (k >> 1) + 16 * (k & 1)>(qr[k], q8);
+      });
+    } else {
+      const uint16_t* qn = a.q_nope + tok * a.q_nope_s_tok + (int64_t)h * a.q_nope_s_head + 8 * (ln >> 5);
+      const uint16_t* qp = a.q_pe + tok * a.q_pe_s_tok + (int64_t)h * a.q_pe_s_head + 8 * (ln >> 5);
+      static_for<32>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        gload16<32 * k>(qr[k], qn);
+      });
+      static_for<4>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        gload16<32 * k>(qr[32 + k], qp);
+      });
+    }
   };
   auto q_landed = [&]() __attribute__((always_inline)) {
     if (32 * w + 32 > RG) {  // wave-uniform: the wave has padding rows
       const bool pad = 32 * w + (lane_now() & 31) >= RG;
 #pragma unroll
-      for (int k = 0; k < 36; ++k)
+      for (int k = 0; k < NQ; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) qr[k][e] = pad ? 0u : qr[k][e];
     }
@@ -464,7 +574,19 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   Cursor pf = first_tile(segs, s_beg, s_end);  // next tile to load
   int issued = 0, done = 0;                    // tiles issued; tiles of finished segments
   int widened = 0;                             // fp8: tiles widened into their bf16 stage
-  if constexpr (FP8) {
+  if constexpr (QF8) {
+    // raw tiles 0..2; the value stages start at zero (the first step of a segment
+    // multiplies P = 0 by the stage of the tile before, which must hold finite values)
+#pragma unroll 1
+    for (int k = 0; k < 3; ++k) {
+      if (pf.si >= s_end) break;
+      dma_q8(dma_tile<true, FAST>(a, pf, smem0 + (issued % kQSlots) * kQSlotB));
+      pf = next_tile(segs, pf, s_end);
+      issued++;
+    }
+#pragma unroll 1
+    for (int i = tid; i < 2 * kStageB / 16; i += 256) *(u32x4_t*)(smem + kQVBase + 16 * i) = u32x4_t{0, 0, 0, 0};
+  } else if constexpr (RAWW) {
     // raw tiles 0 and 1, tile 0 widened into stage 0, raw tile 2 into the freed slot
 #pragma unroll 1
     for (int k = 0; k < 2; ++k) {
@@ -496,7 +618,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   }
   if (has_rows && s_beg < s_end) {
     // the first queries were issued before every DMA load
-    if constexpr (FP8) {
+    if constexpr (QF8) {
+      if (w == 3) wait_tiles<4>(issued);
+      else wait_tiles<5>(issued);
+    } else if constexpr (RAWW) {
       wait_vm<5>();
     } else {
       if (w0) wait_tiles<10>(issued);
@@ -546,8 +671,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
       // fp8: tile s was widened before; this step widens tile s+1 (once: the last step of
       // a segment and the first of the next have the same s) into the stage of tile s-2,
       // then loads the next raw tile into the slot that frees
-      const bool widen_next = FP8 && widened == g + 1 && widened < issued;  // wave-uniform
-      if constexpr (FP8) {
+      const bool widen_next = RAWW && widened == g + 1 && widened < issued;  // wave-uniform
+      if constexpr (QF8) {
+        if (!last) {  // this wave's part of tile s has landed
+          if (w == 3) wait_tiles<4>(issued - g - 1);
+          else wait_tiles<5>(issued - g - 1);
+        }
+        // raw slot of tile g-1 is free after this barrier: tiles up to g+3 may be in flight
+        do_dma = pf.si < s_end && issued < g + kQSlots;
+        if (do_dma) dt = dma_tile<true, FAST>(a, pf, smem0 + ((unsigned)issued % kQSlots) * kQSlotB);
+      } else if constexpr (RAWW) {
         do_dma = pf.si < s_end && issued < widened + (widen_next ? 3 : 2);
         if (do_dma) dt = dma_tile<true, FAST>(a, pf, raw_slot(issued));
       } else {
@@ -561,9 +694,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
         if (do_dma) dt = dma_tile<false, FAST>(a, pf, smem0 + ((unsigned)issued % kStages) * kStageB);
       }
       barrier_lds();  // tile s is in its stage for every wave; the stage of tile s-2 is free
-      const uint32_t qst = ((unsigned)(last ? g - 1 : g) % NST) * kStageB;
-      const uint32_t pst = ((unsigned)(first ? g : g - 1) % NST) * kStageB;
-      const uint32_t wst = ((unsigned)(g + 1) % NST) * kStageB;
+      // QK stage (QF8: raw slot of tile g), P.V stage, stage the widening writes (QF8: the
+      // value stage of tile g, read by the P.V of the next step)
+      const uint32_t qst = QF8 ? ((unsigned)g % kQSlots) * kQSlotB : ((unsigned)(last ? g - 1 : g) % NST) * kStageB;
+      const uint32_t pst = QF8 ? kQVBase + ((unsigned)(g - 1) & 1u) * kStageB
+                               : ((unsigned)(first ? g : g - 1) % NST) * kStageB;
+      const uint32_t wst = QF8 ? kQVBase + ((unsigned)g & 1u) * kStageB : ((unsigned)(g + 1) % NST) * kStageB;
       auto raw_ready = [&]() __attribute__((always_inline)) {
         if (issued > g + 2) wait_vm<5>();  // raw tile s+2 may still be in flight
         else wait_vm<0>();
@@ -571,7 +707,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
       const int tq = ks + kTile * s;  // first key of tile s
 
       if (has_rows && last) {  // the segment's last step has no QK
-        if constexpr (FP8) {
+        if constexpr (QF8) {
+          if (more) issue_q(ld_uniform(segs + 4 * (si + 1)));
+          if (do_dma) dma_q8(dt);
+        } else if constexpr (RAWW) {
           if (widen_next) {
             raw_ready();
             static_for<9>([&](auto ic) __attribute__((always_inline)) { widen(raw_slot(g + 1), wst, ic); });
@@ -589,10 +728,39 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
         // (then it is issued here, with the clamped offsets)
         const bool dma_il = !FP8 && do_dma && (!FAST || dt.kmax >= wkey);  // wave-uniform
         if (!FP8 && !last && do_dma && !dma_il) dma_all(dt);
-        if (FP8 && !last && widen_next) raw_ready();
+        if (RAWW && !last && widen_next) raw_ready();
+        if (QF8 && !last && do_dma) dma_q8(dt);
+        // ---- fp8 queries: S^T = K . Q^T in 9 fp8 k-steps of 64 dims over the raw tile,
+        // with this wave's rows of the tile's value columns widened between them ----
+        if constexpr (QF8) {
+          if (!last) {
+            const char* kp8 = smem + qst + kq8base;
+            auto k8_at = [&](int c) __attribute__((always_inline)) {
+              return cat8(*(const u32x4_t*)(kp8 + 64 * c), *(const u32x4_t*)(kp8 + 64 * c + 16));
+            };
+            constexpr int KR8 = 3;
+            u32x8_t kb8[KR8];
+#pragma unroll
+            for (int c = 0; c < KR8; ++c) kb8[c] = k8_at(c);
+            u32x4_t wr[4];
+            widen8_read(qst, wr);
+            static_for<9>([&](auto kc) __attribute__((always_inline)) {
+              constexpr int c = decltype(kc)::value;
+              const u32x8_t qb = cat8(qr[2 * c], qr[2 * c + 1]);
+              if constexpr (c == 0)
+                mfma8_first(sc, kb8[0], qb);
+              else if constexpr (c == 8)
+                mfma8_last(sc, kb8[c % KR8], qb);
+              else
+                mfma8_acc(sc, kb8[c % KR8], qb);
+              if constexpr (c + KR8 < 9) kb8[c % KR8] = k8_at(c + KR8);
+              if constexpr (c >= 1 && c <= 4) widen8_part(wst, wr, c - 1);
+            });
+          }
+        }
         // ---- S^T[32 keys][32 rows] = K . Q^T: 36 k-steps over the 576 dims, with this
         // wave's DMA of a later tile between the MFMAs ----
-        if (!last) {
+        if (!QF8 && !last) {
           const char* kp = smem + qst + kbase;
           auto k_at = [&](int k) __attribute__((always_inline)) { return *(const u32x4_t*)(kp + 32 * k); };
           constexpr int KR = KRING;
@@ -606,7 +774,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             });
           static_for<36>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
-            if constexpr (k == 0)
+            if constexpr (QF8) {
+              // (not reached: the fp8-query chain above)
+            } else if constexpr (k == 0)
               mfma_v_first_nw(sc, kb[0], qr[0]);
             else if constexpr (k == 35)
               mfma_acc_v_last(sc, kb[k % KR], qr[k]);
@@ -618,10 +788,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
               if (dma_il) dma_one(dt, std::integral_constant<int, n>{});
             }
             // fp8: widen this wave's rows of tile s+1, then load raw tile s+3 into their slot
-            if constexpr (FP8 && k >= 2 && k % 3 == 2 && k / 3 < 9) {
+            if constexpr (RAWW && k >= 2 && k % 3 == 2 && k / 3 < 9) {
               if (widen_next) widen(raw_slot(g + 1), wst, std::integral_constant<int, k / 3>{});
             }
-            if constexpr (FP8 && k == 30) {
+            if constexpr (RAWW && k == 30) {
               if (do_dma) dma_raw(dt);
             }
           });
@@ -741,7 +911,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
           }
         }
       } else {
-        if constexpr (FP8) {
+        if constexpr (QF8) {
+          // no query rows: only this wave's share of the DMA and of the widening
+          if (!last) {
+            u32x4_t wr[4];
+            widen8_read(qst, wr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) widen8_part(wst, wr, i);
+          }
+          if (do_dma) dma_q8(dt);
+        } else if constexpr (RAWW) {
           if (widen_next) {
             raw_ready();
             static_for<9>([&](auto ic) __attribute__((always_inline)) { widen(raw_slot(g + 1), wst, ic); });
@@ -766,7 +945,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
         wait_vm<0>();
       } else if (!dma_last) {
         wait_vm<0>();
-      } else if constexpr (FP8) {
+      } else if constexpr (QF8) {
+        if (w == 3) wait_vm<4>();
+        else wait_vm<5>();
+      } else if constexpr (RAWW) {
         wait_vm<5>();
       } else {
         if (w0) wait_vm<10>();
@@ -825,19 +1007,24 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   wait_vm<0>();  // no DMA outlives the workgroup
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, bool fp8, bool qf8, hipStream_t stream) {
   const int parts8 = (a.num_parts + 7) / 8 * 8;
   const dim3 grid(parts8 * a.head_groups);
   const bool p32 = (a.page_size % 32) == 0;
   if (fp8) {
     const bool canon = (const char*)a.k_pe == (const char*)a.kv_c + kLkv;
-    if (p32 && canon) hipLaunchKernelGGL((mla_decode_pipe_kernel<true, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_pipe_kernel<false, true>), grid, dim3(256), 0, stream, a);
+    if (qf8) {
+      if (p32 && canon) hipLaunchKernelGGL((mla_decode_pipe_kernel<true, true, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((mla_decode_pipe_kernel<false, true, true>), grid, dim3(256), 0, stream, a);
+    } else {
+      if (p32 && canon) hipLaunchKernelGGL((mla_decode_pipe_kernel<true, true, false>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((mla_decode_pipe_kernel<false, true, false>), grid, dim3(256), 0, stream, a);
+    }
   } else {
     // one base for the whole cache row: the rope columns follow the latent ones
     const bool canon = (const char*)a.k_pe == (const char*)a.kv_c + 2 * kLkv;
-    if (p32 && canon) hipLaunchKernelGGL((mla_decode_pipe_kernel<true, false>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_pipe_kernel<false, false>), grid, dim3(256), 0, stream, a);
+    if (p32 && canon) hipLaunchKernelGGL((mla_decode_pipe_kernel<true, false, false>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_pipe_kernel<false, false, false>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

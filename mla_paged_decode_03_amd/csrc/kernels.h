@@ -26,7 +26,9 @@ struct DecodeArgs {
   float* ws_o;                // [partials, Sq*N, 512]
   float* ws_lse;              // [partials, Sq*N]
   float* ws_l;                // [partials, Sq*N]: row sums / kv_scale
-  float qk_scale_log2;        // scale * kv_scale * log2(e)
+  const uint8_t* q8;          // fp8 queries [T, N, 576] e4m3fn (null: bf16 q_nope / q_pe)
+  int64_t q8_s_tok, q8_s_head;  // bytes
+  float qk_scale_log2;        // scale * kv_scale (* q_scale for fp8 queries) * log2(e)
   float out_scale;            // kv_scale
   int32_t Sq, N, page_size, num_parts, head_groups;
 };
@@ -54,7 +56,7 @@ struct QuantArgs {
   int32_t T, N;
 };
 
-hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, bool fp8, bool qf8, hipStream_t stream);
 hipError_t launch_concat_quant_q(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_split_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(void* out, float* out_lse, const void* prefix_o, const float* prefix_lse,

@@ -1,0 +1,114 @@
+"""GPU parity of the fp8-query decode (mla_decode_run_q8) through the C ABI.
+
+The query is quantised on the GPU by mla_concat_quant_q (bit-exact with the oracle's
+quantiser, tests/test_gpu_quant.py); the oracle is fed the same quantised query and the
+identically dequantised fp8 cache.  Cases span the fast (pages of a multiple of 32
+keys) and generic page paths, ragged tails, empty requests, padded row blocks, causal
+verify rows, split and unsplit plans.  Tolerances as for the bf16 query path.
+"""
+import numpy as np
+import pytest
+
+from tests._lib import bf16_dev, bf16_host, ensure_built, u8_dev
+from tests.test_gpu_decode import check, gen_case
+
+pytestmark = pytest.mark.gpu
+ensure_built()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests selected but no GPU is visible")
+    return torch
+
+
+def q_scale_of(inp):
+    """Static per-tensor query scale: max |q| over ql_nope and q_pe, over 448."""
+    from oracle.formats import bf16_to_f64
+    amax = max(np.abs(bf16_to_f64(inp.q)).max(), np.abs(bf16_to_f64(inp.q_pe)).max())
+    return float(np.float32(amax / 448.0))
+
+
+def run_q8(torch, inp, q_scale, num_cus=0, split_phases=False):
+    from mla_paged_decode_03_amd import api
+    w = inp.w
+    T, N = w.T, w.N
+    q8 = torch.empty((T, N, 576), dtype=torch.uint8, device="cuda")
+    api.mla_concat_quant_q(bf16_dev(inp.q), bf16_dev(inp.q_pe), q_scale, q8)
+    cache = u8_dev(inp.cache)
+    bt = torch.from_numpy(inp.block_table).cuda()
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    o = torch.full((T, N, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+    plan = api.mla_decode_plan(inp.seq_lens, w.Sq, N, w.page_size, inp.block_table.shape[1],
+                               api.MLA_DT_FP8_E4M3FN, num_cus)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    if split_phases:
+        api.mla_decode_attend_q8(plan, q8, q_scale, cache, bt, sl, w.scale, inp.kv_scale, o, lse, ws)
+        api.mla_decode_reduce(plan, o, lse, ws)
+    else:
+        api.mla_decode_run_q8(plan, q8, q_scale, cache, bt, sl, w.scale, inp.kv_scale, o, lse, ws)
+    torch.cuda.synchronize()
+    return bf16_host(o), lse.cpu().numpy().astype(np.float64), q8.cpu().numpy()
+
+
+def oracle_q8(inp, q_scale):
+    from oracle import attention as A
+    from oracle import quant as Q
+    from oracle.formats import E4M3FN_TABLE
+    w = inp.w
+    q8 = Q.concat_quant_q(inp.q, inp.q_pe, q_scale)
+    ql = E4M3FN_TABLE[q8[..., :512]] * q_scale
+    qpe = E4M3FN_TABLE[q8[..., 512:]] * q_scale
+    o, lse = A.latent_attention(ql, qpe, inp.cache, "fp8", inp.kv_scale, inp.block_table, inp.seq_lens,
+                                w.Sq, w.scale)
+    return o, lse, q8
+
+
+CASES = [
+    # (N, Sq, page_size, seq_lens, num_cus)
+    (128, 1, 64, [300, 1000], 0),
+    (16, 1, 64, [4000, 100], 6),       # split
+    (128, 4, 64, [257, 2], 3),         # causal verify rows, split
+    (16, 1, 16, [256, 0, 77], 0),      # generic pages, empty request
+    (48, 2, 32, [513, 64, 31], 3),     # padded row blocks, split
+    (100, 1, 7, [50, 13], 2),          # odd page size
+    (8, 8, 64, [200, 10], 0),          # Sq = 8
+    (1, 1, 1, [1, 2, 40], 0),          # one head, page size 1
+]
+
+
+@pytest.mark.parametrize("N,Sq,ps,lens,cus", CASES)
+def test_parity_q8(torch_cuda, N, Sq, ps, lens, cus):
+    inp = gen_case("fp8", seq_lens=np.array(lens, np.int32), B=len(lens), N=N, Sq=Sq, page_size=ps,
+                   pool_pages=None, seed=91 + N + Sq + ps)
+    qs = q_scale_of(inp)
+    o, lse, q8 = run_q8(torch_cuda, inp, qs, num_cus=cus)
+    ro, rl, rq8 = oracle_q8(inp, qs)
+    assert np.array_equal(q8, rq8)
+    check(o, lse, ro, rl, short_rows=min(lens) < 256)
+
+
+def test_attend_then_reduce_equals_run_q8(torch_cuda):
+    inp = gen_case("fp8", seq_lens=np.array([3000, 700, 5], np.int32), B=3, N=128, page_size=64,
+                   pool_pages=None, seed=5)
+    qs = q_scale_of(inp)
+    o1, l1, _ = run_q8(torch_cuda, inp, qs, num_cus=8)
+    o2, l2, _ = run_q8(torch_cuda, inp, qs, num_cus=8, split_phases=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_q8_needs_an_fp8_plan(torch_cuda):
+    from mla_paged_decode_03_amd import api
+    torch = torch_cuda
+    plan = api.mla_decode_plan(np.array([10], np.int32), 1, 16, 16, 1, api.MLA_DT_BF16)
+    q8 = torch.zeros((1, 16, 576), dtype=torch.uint8, device="cuda")
+    cache = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    sl = torch.tensor([10], dtype=torch.int32, device="cuda")
+    o = torch.zeros((1, 16, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(api.MLAError) as e:
+        api.mla_decode_run_q8(plan, q8, 1.0, cache, bt, sl, 0.1, 1.0, o)
+    assert e.value.status in (api.MLA_ERR_UNSUPPORTED, api.MLA_ERR_INVALID_ARG)
