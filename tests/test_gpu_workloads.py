@@ -85,3 +85,45 @@ def test_workload_sampled_parity(torch_cuda, name):
     # every output row is finite (rows not sampled included)
     assert torch.isfinite(o.float()).all()
     plan.destroy()
+
+
+def test_fp8_workload_with_fp8_query_sampled_parity(torch_cuda):
+    """The fp8 workload at full size on the fp8-query path (bench.py --q8): the query is
+    quantised on the GPU with the static scale max|q| / 448; sampled requests are compared
+    with the oracle fed the same quantised query."""
+    torch = torch_cuda
+    from mla_paged_decode_03_amd import api
+    from mla_paged_decode_03_amd import inputs as gen
+    from oracle import attention as A
+    from oracle import quant as Q
+    from oracle.formats import E4M3FN_TABLE, bf16_to_f64
+    w = gen.workload("fp8")
+    inp = gen.generate(w)
+    T, N = w.T, w.N
+    q_scale = float(np.float32(max(np.abs(bf16_to_f64(inp.q)).max(), np.abs(bf16_to_f64(inp.q_pe)).max()) / 448))
+    q8 = torch.empty((T, N, 576), dtype=torch.uint8, device="cuda")
+    api.mla_concat_quant_q(bf16_dev(inp.q), bf16_dev(inp.q_pe), q_scale, q8)
+    cache = u8_dev(inp.cache)
+    bt = torch.from_numpy(inp.block_table).cuda()
+    sl = torch.from_numpy(inp.seq_lens).cuda()
+    o = torch.empty((T, N, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    plan = api.mla_decode_plan(inp.seq_lens, w.Sq, N, w.page_size, inp.block_table.shape[1],
+                               api.MLA_DT_FP8_E4M3FN)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    api.mla_decode_run_q8(plan, q8, q_scale, cache, bt, sl, w.scale, inp.kv_scale, o, lse, ws)
+    torch.cuda.synchronize()
+    reqs = _sample(inp.seq_lens)
+    rq8 = Q.concat_quant_q(inp.q[reqs], inp.q_pe[reqs], q_scale)
+    assert np.array_equal(q8.cpu().numpy()[reqs], rq8)
+    ql = np.zeros((T, N, 512))
+    qpe = np.zeros((T, N, 64))
+    ql[reqs] = E4M3FN_TABLE[rq8[..., :512]] * q_scale
+    qpe[reqs] = E4M3FN_TABLE[rq8[..., 512:]] * q_scale
+    ro, rl = A.latent_attention(ql, qpe, inp.cache, "fp8", inp.kv_scale, inp.block_table, inp.seq_lens,
+                                w.Sq, w.scale, requests=reqs)
+    ma, rel = metrics(bf16_host(o)[reqs], ro[reqs])
+    assert ma <= O_MAX_ABS and rel <= O_REL_L2, (ma, rel)
+    assert np.max(np.abs(lse.cpu().numpy()[reqs] - rl[reqs])) <= LSE_MAX_ABS
+    assert torch.isfinite(o.float()).all()
+    plan.destroy()
