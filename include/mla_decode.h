@@ -242,6 +242,31 @@ int mla_concat_quant_q(const void* ql_nope, int64_t ql_s_tok, int64_t ql_s_head,
                        int64_t qpe_s_tok, int64_t qpe_s_head, float q_scale, void* q8, int64_t q8_s_tok,
                        int64_t q8_s_head, int32_t T, int32_t N, void* stream);
 
+/*
+ * mla_concat_and_cache -- writes new latent rows into the paged cache (vLLM mla/common.py,
+ * MLACommonImpl forward: "write the latent and rope to kv cache" with concat_and_cache_mla
+ * at slot_mapping; for an fp8 cache, quantised with the layer's k_scale).
+ *
+ * Token i with s = slot_mapping[i] writes cache row (s / page_size, s % page_size):
+ *   bf16 cache: [kv_c[i, 0:512] | k_pe[i, 0:64]] copied;
+ *   fp8 cache:  each value x -> e4m3fn(clamp(x * (1 / k_scale), -448, 448)), the reciprocal
+ *               rounded once to fp32, round to nearest even (the stored value times k_scale
+ *               is the cache value the decode reads with kv_scale = k_scale).
+ * Slots outside [0, num_pages * page_size) are skipped; negative slots mark padding
+ * tokens.  Two tokens with the same slot: one of them wins (unspecified which).
+ *
+ *  kv_c [T, 512] bf16 (token stride kv_c_s_tok), k_pe [T, 64] bf16 (k_pe_s_tok),
+ *  slot_mapping [T] int64 (device), cache [num_pages, page_size, 576] (strides in
+ *  elements of the cache dtype; page stride >= page_size * token stride), cache_dtype
+ *  MLA_DT_BF16 or MLA_DT_FP8_E4M3FN, k_scale finite and > 0 for fp8 (unused for bf16).
+ *  Rows and strides 16-byte aligned.
+ * Errors: INVALID_ARG (nulls, sizes, strides, alignment, k_scale), UNSUPPORTED (dtype), HIP.
+ */
+int mla_concat_and_cache(const void* kv_c, int64_t kv_c_s_tok, const void* k_pe, int64_t k_pe_s_tok,
+                         const int64_t* slot_mapping, int32_t T, void* cache, int64_t cache_s_page,
+                         int64_t cache_s_tok, int32_t page_size, int32_t num_pages, int32_t cache_dtype,
+                         float k_scale, void* stream);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* mla_last_error(void);
 

@@ -51,6 +51,7 @@ _SIGS = {
     "mla_plan_export": [_vp, _pi32, _pi32, _pi32, _pi32],
     "mla_debug_gather_rows": [_vp, _vp, _i64, _vp, _vp],
     "mla_concat_quant_q": [_vp, _i64, _i64, _vp, _i64, _i64, _f32, _vp, _i64, _i64, _i32, _i32, _vp],
+    "mla_concat_and_cache": [_vp, _i64, _vp, _i64, _vp, _i32, _vp, _i64, _i64, _i32, _i32, _i32, _f32, _vp],
     "mla_decode_run_q8": [_vp, _vp, _i64, _i64, _f32, _vp, _vp, _i64, _i64, _i32, _vp, _i64, _vp, _f32, _f32,
                           _vp, _i64, _i64, _vp, _vp, _sz, _vp],
     "mla_decode_attend_q8": [_vp, _vp, _i64, _i64, _f32, _vp, _vp, _i64, _i64, _i32, _vp, _i64, _vp, _f32,
@@ -275,6 +276,27 @@ def mla_concat_quant_q(ql_nope, q_pe, q_scale: float, q8, stream=None):
     _check(_lib.mla_concat_quant_q(ql_nope.data_ptr(), ql_nope.stride(0), ql_nope.stride(1),
                                    q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1), float(q_scale),
                                    q8.data_ptr(), q8.stride(0), q8.stride(1), T, N, _stream(stream)))
+
+
+def mla_concat_and_cache(kv_c, k_pe, slot_mapping, cache, k_scale: float = 1.0, stream=None):
+    """kv_c [T,512] bf16, k_pe [T,64] bf16, slot_mapping [T] int64 (device), cache
+    [num_pages, page_size, 576] bf16 or float8_e4m3fn / uint8 (fp8: quantised with k_scale)."""
+    _need(kv_c, (torch.bfloat16,), "kv_c")
+    _need(k_pe, (torch.bfloat16,), "k_pe")
+    _need(slot_mapping, (torch.int64,), "slot_mapping")
+    _need(cache, (torch.bfloat16, torch.float8_e4m3fn, torch.uint8), "cache")
+    T = kv_c.shape[0]
+    if tuple(kv_c.shape) != (T, LKV) or tuple(k_pe.shape) != (T, ROPE) or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("shapes must be kv_c [T,512], k_pe [T,64], slot_mapping [T]")
+    if cache.dim() != 3 or cache.shape[2] != LKV + ROPE or cache.stride(2) != 1:
+        raise ValueError("cache must be [num_pages, page_size, 576] with contiguous rows")
+    if kv_c.stride(1) != 1 or k_pe.stride(1) != 1 or not slot_mapping.is_contiguous():
+        raise ValueError("the last dimension must be contiguous")
+    dt = MLA_DT_BF16 if cache.dtype == torch.bfloat16 else MLA_DT_FP8_E4M3FN
+    _check(_lib.mla_concat_and_cache(kv_c.data_ptr(), kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0),
+                                     slot_mapping.data_ptr(), T, cache.data_ptr(), cache.stride(0),
+                                     cache.stride(1), cache.shape[1], cache.shape[0], dt, float(k_scale),
+                                     _stream(stream)))
 
 
 def mla_plan_compute_host(seq_lens, Sq: int, N: int, num_cus: int):

@@ -502,6 +502,41 @@ int mla_concat_quant_q(const void* ql_nope, int64_t ql_s_tok, int64_t ql_s_head,
   return e == hipSuccess ? MLA_OK : hip_fail(e, "quant launch");
 }
 
+int mla_concat_and_cache(const void* kv_c, int64_t kv_c_s_tok, const void* k_pe, int64_t k_pe_s_tok,
+                         const int64_t* slot_mapping, int32_t T, void* cache, int64_t cache_s_page,
+                         int64_t cache_s_tok, int32_t page_size, int32_t num_pages, int32_t cache_dtype,
+                         float k_scale, void* stream) {
+  if (!kv_c || !k_pe || !slot_mapping || !cache) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (T < 0 || page_size < 1 || num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (cache_dtype != MLA_DT_BF16 && cache_dtype != MLA_DT_FP8_E4M3FN)
+    return fail(MLA_ERR_UNSUPPORTED, "cache_dtype must be MLA_DT_BF16 or MLA_DT_FP8_E4M3FN");
+  const bool fp8 = cache_dtype == MLA_DT_FP8_E4M3FN;
+  if (fp8 && (!std::isfinite(k_scale) || k_scale <= 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "k_scale must be finite and > 0");
+  if (kv_c_s_tok < mla::kLkv || k_pe_s_tok < mla::kRope || cache_s_tok < mla::kHead ||
+      cache_s_page < (int64_t)page_size * cache_s_tok)
+    return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  const int64_t cel = fp8 ? 16 : 8;  // elements per 16 bytes
+  if (!aligned(kv_c, 16) || !aligned(k_pe, 16) || !aligned(cache, 16) || kv_c_s_tok % 8 || k_pe_s_tok % 8 ||
+      cache_s_tok % cel || cache_s_page % cel)
+    return fail(MLA_ERR_INVALID_ARG, "rows must be 16-byte aligned (pointers and strides)");
+  mla::CacheWriteArgs a{};
+  a.kv_c = (const uint16_t*)kv_c;
+  a.kv_c_s_tok = kv_c_s_tok;
+  a.k_pe = (const uint16_t*)k_pe;
+  a.k_pe_s_tok = k_pe_s_tok;
+  a.slot_mapping = slot_mapping;
+  a.cache = cache;
+  a.s_page = cache_s_page;
+  a.s_tok = cache_s_tok;
+  a.inv_scale = fp8 ? 1.0f / k_scale : 1.f;
+  a.T = T;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  hipError_t e = mla::launch_cache_write(a, fp8, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "cache-write launch");
+}
+
 int mla_debug_gather_rows(mla_plan plan, const int32_t* block_table, int64_t block_table_s_req,
                           int64_t* rows_out, void* stream) {
   if (!plan || !block_table || !rows_out) return fail(MLA_ERR_INVALID_ARG, "null pointer");

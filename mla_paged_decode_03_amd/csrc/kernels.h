@@ -56,7 +56,20 @@ struct QuantArgs {
   int32_t T, N;
 };
 
+struct CacheWriteArgs {
+  const uint16_t* kv_c;  // [T, 512] bf16
+  int64_t kv_c_s_tok;
+  const uint16_t* k_pe;  // [T, 64] bf16
+  int64_t k_pe_s_tok;
+  const int64_t* slot_mapping;  // [T]
+  void* cache;                  // [num_pages, page_size, 576] bf16 or e4m3fn
+  int64_t s_page, s_tok;        // elements
+  float inv_scale;              // fp8: 1 / k_scale, rounded once to fp32
+  int32_t T, page_size, num_pages;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, bool fp8, bool qf8, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_concat_quant_q(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_split_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_merge_two(void* out, float* out_lse, const void* prefix_o, const float* prefix_lse,

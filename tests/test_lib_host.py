@@ -149,3 +149,23 @@ def test_concat_quant_argument_errors():
     assert call(q8h=584, q8s=584) == api.MLA_ERR_INVALID_ARG  # not a multiple of 16
     assert call(ql=p16 + 2) == api.MLA_ERR_INVALID_ARG       # misaligned
     assert call(N=0) == api.MLA_ERR_INVALID_ARG
+
+
+def test_concat_and_cache_argument_errors():
+    buf = (C.c_uint8 * 8192)()
+    p16 = (C.cast(buf, C.c_void_p).value + 15) // 16 * 16
+    f = api._lib.mla_concat_and_cache
+    ok = dict(kv=p16, kvs=512, pe=p16, pes=64, sm=p16, T=1, c=p16, cp=576 * 16, ct=576, ps=16, np_=1,
+              dt=api.MLA_DT_BF16, s=1.0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["kv"], a["kvs"], a["pe"], a["pes"], a["sm"], a["T"], a["c"], a["cp"], a["ct"], a["ps"],
+                 a["np_"], a["dt"], a["s"], None)
+    assert call(sm=None) == api.MLA_ERR_INVALID_ARG
+    assert call(dt=api.MLA_DT_FP32) == api.MLA_ERR_UNSUPPORTED
+    assert call(dt=api.MLA_DT_FP8_E4M3FN, s=0.0) == api.MLA_ERR_INVALID_ARG
+    assert call(ct=500) == api.MLA_ERR_INVALID_ARG            # token stride below a row
+    assert call(cp=576) == api.MLA_ERR_INVALID_ARG            # page stride below a page
+    assert call(kv=p16 + 2) == api.MLA_ERR_INVALID_ARG        # misaligned
+    assert call(ps=0) == api.MLA_ERR_INVALID_ARG
