@@ -230,3 +230,66 @@ def random_bf16(seed: int, tid: int, shape, scale: float = 1.0) -> np.ndarray:
 def random_f32(seed: int, tid: int, shape, scale: float = 1.0) -> np.ndarray:
     n = int(np.prod(shape))
     return (np.float32(scale) * _normals(seed, tid, 0, n)).reshape(shape)
+
+
+# ---- chunked prefill -------------------------------------------------------------------
+TID_NEW_KV, TID_NEW_PE = 6, 7
+
+
+@dataclass
+class PrefillInputs:
+    """One chunked-prefill batch: request b has ctx_lens[b] context tokens in the paged
+    cache and new_lens[b] new tokens (rows cu_new[b] .. cu_new[b+1]-1 of the token arrays)."""
+    ctx: Inputs  # cache pool, block_table, kv_scale; ctx.seq_lens = context lengths
+    new_lens: np.ndarray  # [B] int32
+    cu_new: np.ndarray  # [B+1] int32
+    q_nope: np.ndarray  # [T, N, P] bf16 bits
+    q_pe: np.ndarray  # [T, N, R] bf16 bits
+    kv_c: np.ndarray  # [T, 512] bf16 bits (the new tokens' latent rows)
+    k_pe: np.ndarray  # [T, 64] bf16 bits
+    W_UK: np.ndarray  # [512, N, P] bf16 bits
+    W_UV: np.ndarray  # [512, N, V] bf16 bits
+    N: int = 128
+    P: int = 128
+    V: int = 128
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_new[-1])
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.P + ROPE)
+
+
+def generate_prefill(ctx_lens, new_lens, N: int = 128, page_size: int = 64, kv_dtype: str = "bf16",
+                     seed: int = 2000, P: int = 128, V: int = 128) -> PrefillInputs:
+    """Seeded chunked-prefill inputs.  The context cache, block table and fp8 scale are
+    drawn as for a decode batch with seq_lens = ctx_lens (same metadata generator and
+    per-page value generators); the new tokens' q_nope / q_pe / kv_c / k_pe are standard
+    normals (tensor ids 1, 2, 6, 7), W_UK / W_UV 0.02 * standard normals (ids 4, 5), all
+    rounded to bf16."""
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
+    new_lens = np.asarray(new_lens, dtype=np.int32)
+    B = len(ctx_lens)
+    assert new_lens.shape == (B,)
+    w = Workload("prefill", B, 1, N, page_size, kv_dtype, "fixed", 0, 0, P=P, V=V, seed=seed)
+    ctx = generate(w, seq_lens=ctx_lens)
+    ctx.q = None  # the decode query drawn by generate() is not part of a prefill batch
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(new_lens)
+    T = int(cu[-1])
+    nrm = lambda tid, shape, s=1.0: f32_to_bf16_bits(
+        np.float32(s) * _normals(seed, tid, 0, int(np.prod(shape))).reshape(shape))
+    return PrefillInputs(
+        ctx=ctx, new_lens=new_lens, cu_new=cu,
+        q_nope=nrm(TID_Q, (T, N, P)), q_pe=nrm(TID_QPE, (T, N, ROPE)),
+        kv_c=nrm(TID_NEW_KV, (T, LKV)), k_pe=nrm(TID_NEW_PE, (T, ROPE)),
+        W_UK=nrm(TID_WUK, (LKV, N, P), 0.02), W_UV=nrm(TID_WUV, (LKV, N, V), 0.02), N=N, P=P, V=V)
+
+
+# The chunked-prefill workload: DeepSeek-V3 heads (N=128, P=V=128, R=64), 4 requests of
+# 2048 new tokens, each after 6144 tokens of context in 64-token pages, and a context
+# workspace of 8192 tokens (3 chunks of 2048 per request).
+PREFILL_WORKLOAD = dict(ctx_lens=[6144] * 4, new_lens=[2048] * 4, N=128, page_size=64,
+                        kv_dtype="bf16", seed=2001, workspace_tokens=8192)
