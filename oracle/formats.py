@@ -40,3 +40,16 @@ def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "fp8":
         return e4m3fn_to_f64(bits)
     raise ValueError(dtype)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value of each float64 (ties to even), as float64.
+
+    A bfloat16 keeps 8 significant bits: with x = m * 2^e, 0.5 <= |m| < 1, the result is
+    round_half_even(m * 2^8) * 2^(e-8).  Values below the normal bfloat16 range, which the
+    callers never produce, are not treated specially.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+

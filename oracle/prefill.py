@@ -38,7 +38,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import attend, gather_rows
-from .formats import decode
+from .formats import decode, round_to_bf16
 
 
 def chunk_plan(ctx_lens, workspace_tokens: int, page_size: int):
@@ -80,14 +80,23 @@ def context_rows(cache_bits, cache_dtype: str, kv_scale: float, block_table, b: 
     return decode(flat[rows], cache_dtype) * (kv_scale if cache_dtype != "bf16" else 1.0)
 
 
-def kv_b_proj(kv_c: np.ndarray, W_UK: np.ndarray, W_UV: np.ndarray):
+def kv_b_proj(kv_c: np.ndarray, W_UK: np.ndarray, W_UV: np.ndarray, round_to=None):
     """k_nope[s,h,p] = sum_l kv_c[s,l] W_UK[l,h,p];  v[s,h,c] = sum_l kv_c[s,l] W_UV[l,h,c]
-    (docstring "Chunked Prefill": new_k_nope / new_v, cache_k_nope_chunk / cache_v_chunk)."""
+    (docstring "Chunked Prefill": new_k_nope / new_v, cache_k_nope_chunk / cache_v_chunk).
+
+    round_to="bf16" rounds both results to bfloat16 (ties to even): the pages materialise
+    k_nope and v as the output of the kv_b_proj linear layer, in the model's dtype
+    (``_compute_prefill_context`` and ``forward_mha`` split ``kv_b_proj(...)``), so every
+    logit of that pipeline is taken against the rounded keys."""
     Lkv, N, P = W_UK.shape
     V = W_UV.shape[2]
     S = kv_c.shape[0]
     k_nope = (kv_c @ W_UK.reshape(Lkv, N * P)).reshape(S, N, P)
     v = (kv_c @ W_UV.reshape(Lkv, N * V)).reshape(S, N, V)
+    if round_to == "bf16":
+        k_nope, v = round_to_bf16(k_nope), round_to_bf16(v)
+    elif round_to is not None:
+        raise ValueError(round_to)
     return k_nope, v
 
 
@@ -114,7 +123,8 @@ def mha(q_nope, q_pe, k_nope, k_pe, v, scale: float, causal: bool):
 
 
 def chunked_prefill(q_nope, q_pe, cu_new, kv_c, k_pe, ctx_lens, cache_bits, cache_dtype: str,
-                    kv_scale: float, block_table, W_UK, W_UV, scale: float, requests=None):
+                    kv_scale: float, block_table, W_UK, W_UV, scale: float, requests=None,
+                    kv_round=None):
     """Output of a chunked-prefill batch, by the definition.
 
     q_nope [T, N, P], q_pe [T, N, R], kv_c [T, Lkv], k_pe [T, R] (float64, the T new tokens,
@@ -122,6 +132,11 @@ def chunked_prefill(q_nope, q_pe, cu_new, kv_c, k_pe, ctx_lens, cache_bits, cach
     latent rows are in the paged cache ``cache_bits`` [pages, ps, Lkv+R] through
     ``block_table``.  Returns o [T, N, V], lse [T, N]; rows of requests not listed in
     ``requests`` are NaN.
+
+    kv_round="bf16" keeps the pipeline's intermediate tensors in the model dtype, as the
+    pages hold them: the dequantised context rows (the bf16 workspace that
+    ``gather_and_maybe_dequant_cache`` fills) and k_nope, v (the output of ``kv_b_proj``),
+    each rounded to bfloat16, ties to even.  None computes the definition unrounded.
     """
     Lkv = W_UK.shape[0]
     T, N, _ = q_nope.shape
@@ -133,8 +148,10 @@ def chunked_prefill(q_nope, q_pe, cu_new, kv_c, k_pe, ctx_lens, cache_bits, cach
         lo, hi = int(cu_new[b]), int(cu_new[b + 1])
         C = int(ctx_lens[b])
         ctx = context_rows(cache_bits, cache_dtype, kv_scale, block_table, b, 0, C)
+        if kv_round == "bf16":
+            ctx = round_to_bf16(ctx)
         lat = np.concatenate([ctx[:, :Lkv], kv_c[lo:hi]], axis=0)
         pe = np.concatenate([ctx[:, Lkv:], k_pe[lo:hi]], axis=0)
-        k_nope, v = kv_b_proj(lat, W_UK, W_UV)
+        k_nope, v = kv_b_proj(lat, W_UK, W_UV, round_to=kv_round)
         o[lo:hi], lse[lo:hi] = mha(q_nope[lo:hi], q_pe[lo:hi], k_nope, pe, v, scale, causal=True)
     return o, lse

@@ -77,3 +77,22 @@ def test_generator_seq_len_recipes():
     assert gen.draw_seq_lens(gen.workload("longtail"),
                              np.random.Generator(np.random.PCG64(1002))).tolist() == \
         np.clip(np.floor(np.exp(u)), 512, 32768).astype(int).tolist()
+
+
+def test_round_to_bf16_against_torch_and_ties():
+    """Nearest bfloat16, ties to even: torch's float32 -> bfloat16 conversion on random
+    float32 values of many magnitudes (torch converts float64 through float32, a double
+    rounding, so the comparison uses float32 inputs), and exact midpoints built by hand."""
+    import torch
+    from oracle.formats import round_to_bf16
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(200_000) * np.exp2(rng.integers(-30, 30, 200_000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(round_to_bf16(x.astype(np.float64)), ref)
+    one_ulp = 2.0 ** -7  # spacing of bfloat16 in [1, 2)
+    assert round_to_bf16(np.array([1 + one_ulp / 2]))[0] == 1.0  # tie -> even (1.0)
+    assert round_to_bf16(np.array([1 + 3 * one_ulp / 2]))[0] == 1 + 2 * one_ulp  # tie -> even
+    assert round_to_bf16(np.array([-(1 + 3 * one_ulp / 2)]))[0] == -(1 + 2 * one_ulp)
+    assert round_to_bf16(np.array([1 + one_ulp / 2 + 2.0 ** -40]))[0] == 1 + one_ulp
+    assert round_to_bf16(np.array([0.0]))[0] == 0.0
+

@@ -192,3 +192,32 @@ def test_fp8_context_is_dequantised_with_the_scale():
     ref = torch.from_numpy(codes.reshape(-1, 20)).view(torch.float8_e4m3fn).double().numpy() * 0.5
     flat_rows = [1 * 4 + 2, 1 * 4 + 3, 0 * 4 + 0, 0 * 4 + 1, 0 * 4 + 2]
     np.testing.assert_array_equal(rows, ref[flat_rows])
+
+
+def test_rounded_pipeline_is_exact_when_nothing_rounds():
+    """kv_round="bf16" only rounds the intermediate tensors: with W_UK / W_UV selecting
+    single latent columns (k_nope and v are copies of bf16 cache values) nothing changes."""
+    rng = np.random.default_rng(23)
+    ctx_lens, new_lens = [9, 0, 23], [5, 3, 1]
+    c = _case(rng, ctx_lens, new_lens)
+    Lkv, N, P = c["W_UK"].shape
+    V = c["W_UV"].shape[2]
+    from oracle.formats import round_to_bf16
+    c["kv_c"] = round_to_bf16(c["kv_c"])
+    wk = np.zeros((Lkv, N, P))
+    wv = np.zeros((Lkv, N, V))
+    for h in range(N):
+        for p in range(P):
+            wk[(3 * h + p) % Lkv, h, p] = 1.0
+        for q in range(V):
+            wv[(5 * h + q) % Lkv, h, q] = 1.0
+    c["W_UK"], c["W_UV"] = wk, wv
+    o0, l0 = PF.chunked_prefill(**c)
+    o1, l1 = PF.chunked_prefill(**c, kv_round="bf16")
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    # and with general weights the rounded pipeline moves the output by about a bf16 step
+    c2 = _case(np.random.default_rng(24), ctx_lens, new_lens)
+    o0, _ = PF.chunked_prefill(**c2)
+    o1, _ = PF.chunked_prefill(**c2, kv_round="bf16")
+    assert 0 < np.max(np.abs(o1 - o0)) < 2.0 ** -5 * max(1.0, np.max(np.abs(o0)))
+
