@@ -267,6 +267,103 @@ int mla_concat_and_cache(const void* kv_c, int64_t kv_c_s_tok, const void* k_pe,
                          int64_t cache_s_tok, int32_t page_size, int32_t num_pages, int32_t cache_dtype,
                          float k_scale, void* stream);
 
+/* ---- chunked prefill, compute-friendly form ----
+ *
+ * vLLM mla/common.py module docstring, "Chunked Prefill": keys and values are
+ * up-projected per head from the latent rows (k_nope = kv_c W_UK, v = kv_c W_UV),
+ * k_pe is shared by all heads, and each head runs attention with QK width P+R and
+ * value width V.  The context is visited in chunks (MLACommonImpl.
+ * _compute_prefill_context: gather and dequantise the chunk's cache rows, kv_b_proj,
+ * attention without a mask), chunk outputs are combined by merge_attn_states, and
+ * the new tokens attend to themselves causally (forward_mha), the last merge taking
+ * the context output as prefix and the new tokens' output as suffix.
+ * Supported: Lkv = 512, R = 64, P = V = 128 (DeepSeek-V3 head dims).
+ */
+
+/*
+ * mla_prefill_attention -- per-head softmax attention of requests laid out back to
+ * back.  Request b owns queries cu_q[b]..cu_q[b+1]-1 and keys cu_k[b]..cu_k[b+1]-1
+ * (cu_q, cu_k: device int32 [B+1], non-decreasing from 0); causal != 0: query i of
+ * the request (0-based) sees keys j <= i + Sk_b - Sq_b (the new tokens are the last
+ * keys), otherwise all Sk_b keys.
+ *  q_nope [T,N,P], q_pe [T,N,R], k_nope [S,N,P], k_pe [S,R] (one rope row per key,
+ *  shared by the heads), v [S,N,V]: bf16, strides in elements (token, head), rows
+ *  16-byte aligned.  max_q >= max_b Sq_b.  scale multiplies the logits.
+ *  o [T,N,V] bf16 receives sum softmax * v; lse [T,N] fp32 (t*N + h, natural log,
+ *  scale included) or NULL.  A query with no key gets o = 0, lse = -inf.
+ * Errors: INVALID_ARG (null pointers, strides, alignment), UNSUPPORTED (P, R, V),
+ * HIP.  Enqueued on stream; no allocation, no host synchronisation.
+ */
+int mla_prefill_attention(const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head, const void* q_pe,
+                          int64_t q_pe_s_tok, int64_t q_pe_s_head, const void* k_nope, int64_t k_nope_s_tok,
+                          int64_t k_nope_s_head, const void* k_pe, int64_t k_pe_s_tok, const void* v,
+                          int64_t v_s_tok, int64_t v_s_head, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
+                          int32_t max_q, int32_t N, int32_t P, int32_t R, int32_t V, int32_t causal, float scale,
+                          void* o, int64_t o_s_tok, int64_t o_s_head, float* lse, void* stream);
+
+/*
+ * mla_gather_context -- one context chunk of the paged cache into contiguous rows
+ * (mla/common.py, _compute_prefill_context: gather_and_maybe_dequant_cache).
+ * Output row r, for the request b with cu[b] <= r < cu[b+1], is context position
+ * p = starts[b] + r - cu[b] of that request: cache row
+ * block_table[b][p / page_size], slot p % page_size.  out_kv_c [total,512] and
+ * out_k_pe [total,64] bf16 (row strides in elements); fp8 caches are widened and
+ * multiplied by kv_scale in fp32, then rounded to bf16 (nearest even).
+ * starts [B], cu [B+1]: device int32.  Cache pointers and strides as mla_decode_run.
+ * Block-table entries of the positions read must be valid pages (not checked).
+ */
+int mla_gather_context(const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page, int64_t cache_s_tok,
+                       int32_t page_size, int32_t kv_dtype, float kv_scale, const int32_t* block_table,
+                       int64_t block_table_s_req, const int32_t* starts, const int32_t* cu, int32_t B,
+                       int64_t total, void* out_kv_c, int64_t out_kv_c_s_tok, void* out_k_pe,
+                       int64_t out_k_pe_s_tok, void* stream);
+
+/*
+ * mla_kv_b_proj -- k_nope[s,h,p] = sum_l kv_c[s,l] W_UK[l,h,p] and
+ * v[s,h,c] = sum_l kv_c[s,l] W_UV[l,h,c] (the docstring's kv_b_proj split into its
+ * W_UK and W_UV parts): kv_c [S,Lkv] bf16 (row stride kv_c_s_tok), W_UK [Lkv,N,P],
+ * W_UV [Lkv,N,V], k_nope [S,N,P], v [S,N,V] contiguous bf16; fp32 accumulation,
+ * outputs rounded to nearest even.
+ */
+int mla_kv_b_proj(const void* kv_c, int64_t kv_c_s_tok, const void* W_UK, const void* W_UV, void* k_nope,
+                  void* v, int32_t S, int32_t N, int32_t Lkv, int32_t P, int32_t V, void* stream);
+
+/*
+ * mla_chunked_prefill_workspace_size -- bytes of device workspace mla_chunked_prefill
+ * needs for these host counts (new tokens and context tokens per request), head
+ * shape and context workspace of workspace_tokens latent rows.
+ * The chunk schedule (MLACommonMetadataBuilder, chunked context): with k requests
+ * that have context, mcc = workspace_tokens / k rounded down to a multiple of
+ * page_size (kept when smaller than a page); chunk i of request b covers context
+ * positions [i*mcc, min((i+1)*mcc, ctx_lens[b])).  WORKSPACE if mcc would be 0.
+ */
+int mla_chunked_prefill_workspace_size(const int32_t* new_lens_host, const int32_t* ctx_lens_host, int32_t B,
+                                       int32_t N, int32_t P, int32_t V, int32_t page_size,
+                                       int64_t workspace_tokens, size_t* workspace_bytes_out);
+
+/*
+ * mla_chunked_prefill -- output of a prefill batch: request b has ctx_lens[b] tokens
+ * of context in the paged cache and new_lens[b] new tokens (rows laid out back to
+ * back in request order, T = sum new_lens); new token i of request b sees every
+ * context key and the new keys 0..i.
+ *  q_nope [T,N,P], q_pe [T,N,R], kv_c [T,Lkv], k_pe [T,R]: the new tokens' queries
+ *  and latent rows, contiguous bf16.  new_lens_host, ctx_lens_host: host int32 [B].
+ *  Cache, block_table, kv_dtype and kv_scale as mla_decode_run.  W_UK, W_UV
+ *  [Lkv,N,P] / [Lkv,N,V] contiguous bf16.  o [T,N,V] bf16 contiguous; lse [T,N] or
+ *  NULL.  workspace: device, 256-byte aligned, of the size above.
+ * Launches, in order: kv_b_proj and causal attention of the new tokens, then per
+ * chunk gather, kv_b_proj, attention and a merge, then the final merge; all on
+ * stream.  The chunk schedule goes to the workspace by one host-to-device copy
+ * from pageable memory.  Errors as the calls above, WORKSPACE if too small.
+ */
+int mla_chunked_prefill(const void* q_nope, const void* q_pe, const void* kv_c, const void* k_pe,
+                        const int32_t* new_lens_host, const int32_t* ctx_lens_host, int32_t B, const void* cache_kv_c,
+                        const void* cache_k_pe, int64_t cache_s_page, int64_t cache_s_tok, int32_t page_size,
+                        int32_t kv_dtype, float kv_scale, const int32_t* block_table, int64_t block_table_s_req,
+                        const void* W_UK, const void* W_UV, int32_t N, int32_t Lkv, int32_t P, int32_t R,
+                        int32_t V, float scale, int64_t workspace_tokens, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* mla_last_error(void);
 

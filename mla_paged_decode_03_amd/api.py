@@ -56,6 +56,15 @@ _SIGS = {
                           _vp, _i64, _i64, _vp, _vp, _sz, _vp],
     "mla_decode_attend_q8": [_vp, _vp, _i64, _i64, _f32, _vp, _vp, _i64, _i64, _i32, _vp, _i64, _vp, _f32,
                              _f32, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mla_prefill_attention": [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
+                              _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _i64, _i64, _vp,
+                              _vp],
+    "mla_gather_context": [_vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64,
+                           _vp, _i64, _vp],
+    "mla_kv_b_proj": [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
+    "mla_chunked_prefill_workspace_size": [_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i64, C.POINTER(_sz)],
+    "mla_chunked_prefill": [_vp, _vp, _vp, _vp, _pi32, _pi32, _i32, _vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp,
+                            _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i64, _vp, _vp, _vp, _sz, _vp],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -329,6 +338,103 @@ def mla_debug_gather_rows(plan: Plan, block_table, rows_out, stream=None):
     _need(rows_out, (torch.int64,), "rows_out")
     _check(_lib.mla_debug_gather_rows(plan.handle, block_table.data_ptr(), block_table.stride(0),
                                       rows_out.data_ptr(), _stream(stream)))
+
+
+def _rows16(t, name):
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+
+
+def mla_prefill_attention(q_nope, q_pe, k_nope, k_pe, v, cu_q, cu_k, max_q: int, causal: bool,
+                          scale: float, o, lse=None, stream=None):
+    """Per-head attention of the compute-friendly path: q_nope [T,N,128], q_pe [T,N,64],
+    k_nope [S,N,128], k_pe [S,64] (shared by the heads), v [S,N,128] bf16; cu_q / cu_k
+    [B+1] int32 device offsets of each request's queries and keys; o [T,N,128] bf16,
+    lse [T,N] fp32 or None."""
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (k_nope, "k_nope"), (k_pe, "k_pe"), (v, "v"), (o, "o")):
+        _need(t, (torch.bfloat16,), n)
+        _rows16(t, n)
+    for t, n in ((cu_q, "cu_q"), (cu_k, "cu_k")):
+        _need(t, (torch.int32,), n)
+    if lse is not None:
+        _need(lse, (torch.float32,), "lse")
+        if not lse.is_contiguous():
+            raise ValueError("lse must be contiguous [T, N]")
+    T, N, P = q_nope.shape
+    B = cu_q.shape[0] - 1
+    _check(_lib.mla_prefill_attention(
+        q_nope.data_ptr(), q_nope.stride(0), q_nope.stride(1), q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1),
+        k_nope.data_ptr(), k_nope.stride(0), k_nope.stride(1), k_pe.data_ptr(), k_pe.stride(0),
+        v.data_ptr(), v.stride(0), v.stride(1), cu_q.data_ptr(), cu_k.data_ptr(), B, int(max_q), N, P,
+        q_pe.shape[2], v.shape[2], int(bool(causal)), float(scale), o.data_ptr(), o.stride(0), o.stride(1),
+        _ptr(lse), _stream(stream)))
+
+
+def mla_gather_context(cache, block_table, starts, cu, total: int, out_kv_c, out_k_pe,
+                       kv_scale: float = 1.0, stream=None):
+    """Rows of one context chunk: out row r of request b (cu[b] <= r < cu[b+1]) is the
+    cache row of position starts[b] + r - cu[b]; bf16 out_kv_c [n,512], out_k_pe [n,64]."""
+    _need(cache, (torch.bfloat16, torch.float8_e4m3fn, torch.uint8), "cache")
+    for t, n in ((block_table, "block_table"), (starts, "starts"), (cu, "cu")):
+        _need(t, (torch.int32,), n)
+    _need(out_kv_c, (torch.bfloat16,), "out_kv_c")
+    _need(out_k_pe, (torch.bfloat16,), "out_k_pe")
+    if cache.dim() != 3 or cache.shape[2] != LKV + ROPE or cache.stride(2) != 1:
+        raise ValueError("cache must be [num_pages, page_size, 576] with contiguous rows")
+    dt = MLA_DT_BF16 if cache.dtype == torch.bfloat16 else MLA_DT_FP8_E4M3FN
+    kpe = cache.data_ptr() + LKV * cache.element_size()
+    _check(_lib.mla_gather_context(cache.data_ptr(), kpe, cache.stride(0), cache.stride(1), cache.shape[1], dt,
+                                   float(kv_scale), block_table.data_ptr(), block_table.stride(0),
+                                   starts.data_ptr(), cu.data_ptr(), starts.shape[0], int(total),
+                                   out_kv_c.data_ptr(), out_kv_c.stride(0), out_k_pe.data_ptr(),
+                                   out_k_pe.stride(0), _stream(stream)))
+
+
+def mla_kv_b_proj(kv_c, W_UK, W_UV, k_nope, v, stream=None):
+    """k_nope[s,h,:] = kv_c[s] . W_UK[:,h,:], v[s,h,:] = kv_c[s] . W_UV[:,h,:] (bf16)."""
+    _need_contig_bf16(W_UK, W_UV, k_nope, v)
+    _need(kv_c, (torch.bfloat16,), "kv_c")
+    _rows16(kv_c, "kv_c")
+    S, Lkv = kv_c.shape
+    _, N, P = W_UK.shape
+    V = W_UV.shape[2]
+    _check(_lib.mla_kv_b_proj(kv_c.data_ptr(), kv_c.stride(0), W_UK.data_ptr(), W_UV.data_ptr(),
+                              k_nope.data_ptr(), v.data_ptr(), S, N, Lkv, P, V, _stream(stream)))
+
+
+def mla_chunked_prefill_workspace_size(new_lens, ctx_lens, N: int, P: int, V: int, page_size: int,
+                                       workspace_tokens: int) -> int:
+    nl, cl = _host_i32(new_lens), _host_i32(ctx_lens)
+    out = _sz(0)
+    _check(_lib.mla_chunked_prefill_workspace_size(nl.ctypes.data_as(_pi32), cl.ctypes.data_as(_pi32), len(nl),
+                                                   N, P, V, page_size, int(workspace_tokens), C.byref(out)))
+    return out.value
+
+
+def mla_chunked_prefill(q_nope, q_pe, kv_c, k_pe, new_lens, ctx_lens, cache, block_table, W_UK, W_UV,
+                        scale: float, workspace_tokens: int, o, lse=None, workspace=None, kv_scale: float = 1.0,
+                        stream=None):
+    """Chunked prefill of a batch (compute-friendly form): new tokens q_nope [T,N,128],
+    q_pe [T,N,64], their latent rows kv_c [T,512] and k_pe [T,64] (contiguous bf16);
+    new_lens / ctx_lens [B] host counts; context in the paged cache through block_table;
+    W_UK / W_UV [512,N,128]; o [T,N,128] bf16, lse [T,N] fp32 or None."""
+    _need_contig_bf16(q_nope, q_pe, kv_c, k_pe, W_UK, W_UV, o)
+    _need(cache, (torch.bfloat16, torch.float8_e4m3fn, torch.uint8), "cache")
+    _need(block_table, (torch.int32,), "block_table")
+    if lse is not None:
+        _need(lse, (torch.float32,), "lse")
+    nl, cl = _host_i32(new_lens), _host_i32(ctx_lens)
+    T, N, P = q_nope.shape
+    V = W_UV.shape[2]
+    dt = MLA_DT_BF16 if cache.dtype == torch.bfloat16 else MLA_DT_FP8_E4M3FN
+    kpe = cache.data_ptr() + LKV * cache.element_size()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.mla_chunked_prefill(
+        q_nope.data_ptr(), q_pe.data_ptr(), kv_c.data_ptr(), k_pe.data_ptr(), nl.ctypes.data_as(_pi32),
+        cl.ctypes.data_as(_pi32), len(nl), cache.data_ptr(), kpe, cache.stride(0), cache.stride(1),
+        cache.shape[1], dt, float(kv_scale), block_table.data_ptr(), block_table.stride(0), W_UK.data_ptr(),
+        W_UV.data_ptr(), N, W_UK.shape[0], P, q_pe.shape[2], V, float(scale), int(workspace_tokens),
+        o.data_ptr(), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def exported_symbols():

@@ -1,6 +1,7 @@
 // C ABI of the library: argument validation, plans, launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -545,6 +546,313 @@ int mla_debug_gather_rows(mla_plan plan, const int32_t* block_table, int64_t blo
                                          (const int64_t*)(plan->d_buf + plan->off_offsets), plan->host.B,
                                          plan->page_size, rows_out, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : hip_fail(e, "gather-rows launch");
+}
+
+// ---------------------------------------------------------------------------------
+// Chunked prefill (compute-friendly form)
+// ---------------------------------------------------------------------------------
+
+int mla_prefill_attention(const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head, const void* q_pe,
+                          int64_t q_pe_s_tok, int64_t q_pe_s_head, const void* k_nope, int64_t k_nope_s_tok,
+                          int64_t k_nope_s_head, const void* k_pe, int64_t k_pe_s_tok, const void* v,
+                          int64_t v_s_tok, int64_t v_s_head, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
+                          int32_t max_q, int32_t N, int32_t P, int32_t R, int32_t V, int32_t causal, float scale,
+                          void* o, int64_t o_s_tok, int64_t o_s_head, float* lse, void* stream) {
+  if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !cu_q || !cu_k || !o)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (B < 0 || B > 65535 || max_q < 0 || N < 1 || N > 65535) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (P != 128 || R != mla::kRope || V != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "only P = 128, R = 64 and V = 128 are supported");
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  if (q_nope_s_head < P || q_pe_s_head < R || k_nope_s_head < P || v_s_head < V || o_s_head < V ||
+      q_nope_s_tok < (int64_t)N * q_nope_s_head || q_pe_s_tok < (int64_t)N * q_pe_s_head ||
+      k_nope_s_tok < (int64_t)N * k_nope_s_head || k_pe_s_tok < R || v_s_tok < (int64_t)N * v_s_head ||
+      o_s_tok < (int64_t)N * o_s_head)
+    return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  const int64_t st[] = {q_nope_s_tok, q_nope_s_head, q_pe_s_tok, q_pe_s_head, k_nope_s_tok, k_nope_s_head,
+                        k_pe_s_tok, v_s_tok, v_s_head, o_s_tok, o_s_head};
+  for (int64_t x : st)
+    if (x % 8) return fail(MLA_ERR_INVALID_ARG, "rows must be 16-byte aligned (strides)");
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(k_nope, 16) || !aligned(k_pe, 16) ||
+      !aligned(v, 16) || !aligned(o, 16))
+    return fail(MLA_ERR_INVALID_ARG, "rows must be 16-byte aligned (pointers)");
+  mla::PrefillAttnArgs a{};
+  a.q_nope = (const uint16_t*)q_nope;
+  a.qn_s_tok = q_nope_s_tok;
+  a.qn_s_head = q_nope_s_head;
+  a.q_pe = (const uint16_t*)q_pe;
+  a.qp_s_tok = q_pe_s_tok;
+  a.qp_s_head = q_pe_s_head;
+  a.k_nope = (const uint16_t*)k_nope;
+  a.kn_s_tok = k_nope_s_tok;
+  a.kn_s_head = k_nope_s_head;
+  a.k_pe = (const uint16_t*)k_pe;
+  a.kp_s_tok = k_pe_s_tok;
+  a.v = (const uint16_t*)v;
+  a.v_s_tok = v_s_tok;
+  a.v_s_head = v_s_head;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.o = (uint16_t*)o;
+  a.o_s_tok = o_s_tok;
+  a.o_s_head = o_s_head;
+  a.lse = lse;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.N = N;
+  a.causal = causal ? 1 : 0;
+  hipError_t e = mla::launch_prefill_attn(a, B, max_q, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "prefill attention launch");
+}
+
+int mla_gather_context(const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page, int64_t cache_s_tok,
+                       int32_t page_size, int32_t kv_dtype, float kv_scale, const int32_t* block_table,
+                       int64_t block_table_s_req, const int32_t* starts, const int32_t* cu, int32_t B,
+                       int64_t total, void* out_kv_c, int64_t out_kv_c_s_tok, void* out_k_pe,
+                       int64_t out_k_pe_s_tok, void* stream) {
+  if (!cache_kv_c || !cache_k_pe || !block_table || !starts || !cu || !out_kv_c || !out_k_pe)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || total < 0 || page_size < 1) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (kv_dtype != MLA_DT_BF16 && kv_dtype != MLA_DT_FP8_E4M3FN)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_dtype must be MLA_DT_BF16 or MLA_DT_FP8_E4M3FN");
+  const bool fp8 = kv_dtype == MLA_DT_FP8_E4M3FN;
+  if (fp8 && (!std::isfinite(kv_scale) || kv_scale <= 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "kv_scale must be finite and > 0");
+  if (cache_s_tok < mla::kHead || cache_s_page < (int64_t)page_size * cache_s_tok || out_kv_c_s_tok < mla::kLkv ||
+      out_k_pe_s_tok < mla::kRope)
+    return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  const int64_t cel = fp8 ? 8 : 8;  // bf16: 16-byte chunks; fp8: 8-byte chunks of 8 values
+  if (!aligned(cache_kv_c, fp8 ? 8 : 16) || !aligned(cache_k_pe, fp8 ? 8 : 16) || !aligned(out_kv_c, 16) ||
+      !aligned(out_k_pe, 16) || cache_s_tok % cel || cache_s_page % cel || out_kv_c_s_tok % 8 ||
+      out_k_pe_s_tok % 8)
+    return fail(MLA_ERR_INVALID_ARG, "rows must be aligned (pointers and strides)");
+  mla::GatherArgs a{};
+  a.kv_c = cache_kv_c;
+  a.k_pe = cache_k_pe;
+  a.s_page = cache_s_page;
+  a.s_tok = cache_s_tok;
+  a.block_table = block_table;
+  a.bt_s = block_table_s_req;
+  a.starts = starts;
+  a.cu = cu;
+  a.out_kv_c = (uint16_t*)out_kv_c;
+  a.okv_s = out_kv_c_s_tok;
+  a.out_k_pe = (uint16_t*)out_k_pe;
+  a.ope_s = out_k_pe_s_tok;
+  a.kv_scale = fp8 ? kv_scale : 1.f;
+  a.total = total;
+  a.B = B;
+  a.page_size = page_size;
+  hipError_t e = mla::launch_gather_ctx(a, fp8, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "context gather launch");
+}
+
+int mla_kv_b_proj(const void* kv_c, int64_t kv_c_s_tok, const void* W_UK, const void* W_UV, void* k_nope,
+                  void* v, int32_t S, int32_t N, int32_t Lkv, int32_t P, int32_t V, void* stream) {
+  if (!kv_c || !W_UK || !W_UV || !k_nope || !v) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (S < 0 || N < 1 || P < 8 || V < 8 || Lkv < 8) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (P % 8 || V % 8 || Lkv % 8) return fail(MLA_ERR_UNSUPPORTED, "P, V and Lkv must be multiples of 8");
+  if (kv_c_s_tok < Lkv || kv_c_s_tok % 8) return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  if (!aligned(kv_c, 16) || !aligned(W_UK, 16) || !aligned(W_UV, 16) || !aligned(k_nope, 16) || !aligned(v, 16))
+    return fail(MLA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  for (int which = 0; which < 2; ++which) {
+    const int32_t W = which ? V : P;
+    mla::GemmArgs g{};
+    g.A = (const uint16_t*)kv_c;  // (h, m=s, k=l) at s*kv_c_s_tok + l: shared by the heads
+    g.a_sh = 0;
+    g.a_sm = kv_c_s_tok;
+    g.B = (const uint16_t*)(which ? W_UV : W_UK);  // (h, n, k=l) at l*N*W + h*W + n
+    g.b_sh = W;
+    g.b_sn = 1;
+    g.b_sk = (int64_t)N * W;
+    g.C = (uint16_t*)(which ? v : k_nope);  // (h, s, n) at s*N*W + h*W + n
+    g.c_sh = W;
+    g.c_sm = (int64_t)N * W;
+    g.H = N;
+    g.M = S;
+    g.Nn = W;
+    g.K = Lkv;
+    hipError_t e = mla::launch_gemm(g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_b_proj launch");
+  }
+  return MLA_OK;
+}
+
+namespace {
+
+// Chunk schedule of the context (mla/common.py, MLACommonMetadataBuilder, chunked
+// context): the workspace is split evenly over the requests that have context, rounded
+// down to a multiple of the page size; chunk i of request b covers positions
+// [i*mcc, min((i+1)*mcc, C_b)).
+struct ChunkSched {
+  int64_t mcc = 0;
+  int n = 0;
+  std::vector<int32_t> starts, cu;  // [n][B], [n][B+1]
+  int64_t max_total = 0;
+};
+
+int chunk_schedule(const int32_t* ctx, int32_t B, int32_t page_size, int64_t workspace_tokens, ChunkSched& cs) {
+  int64_t with_ctx = 0, cmax = 0;
+  for (int b = 0; b < B; ++b) {
+    if (ctx[b] < 0) return fail(MLA_ERR_INVALID_ARG, "negative context length");
+    with_ctx += ctx[b] > 0;
+    cmax = std::max<int64_t>(cmax, ctx[b]);
+  }
+  cs = ChunkSched{};
+  if (with_ctx == 0) return MLA_OK;
+  int64_t mcc = workspace_tokens / with_ctx;
+  if (mcc >= page_size) mcc = mcc / page_size * page_size;
+  if (mcc <= 0) return fail(MLA_ERR_WORKSPACE, "workspace_tokens smaller than the number of requests with context");
+  cs.mcc = mcc;
+  cs.n = (int)((cmax + mcc - 1) / mcc);
+  cs.starts.assign((size_t)cs.n * B, 0);
+  cs.cu.assign((size_t)cs.n * (B + 1), 0);
+  for (int i = 0; i < cs.n; ++i) {
+    int64_t acc = 0;
+    for (int b = 0; b < B; ++b) {
+      const int64_t st = (int64_t)i * mcc, en = std::min<int64_t>(ctx[b], st + mcc);
+      cs.starts[(size_t)i * B + b] = (int32_t)st;
+      cs.cu[(size_t)i * (B + 1) + b] = (int32_t)acc;
+      acc += std::max<int64_t>(0, en - st);
+    }
+    cs.cu[(size_t)i * (B + 1) + B] = (int32_t)acc;
+    cs.max_total = std::max(cs.max_total, acc);
+  }
+  return MLA_OK;
+}
+
+struct PrefillLayout {
+  size_t meta, lat_kv, lat_pe, kn, vv, o_new, l_new, o_ctx, l_ctx, o_chk, l_chk, total;
+};
+
+PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t N, int32_t P, int32_t V, const ChunkSched& cs) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  PrefillLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  const int64_t S = std::max<int64_t>(T, cs.max_total);
+  const bool ctx = cs.n > 0;
+  L.meta = take(sizeof(int32_t) * ((size_t)(B + 1) + (size_t)cs.n * (2 * B + 1)));
+  L.lat_kv = take(ctx ? (size_t)cs.max_total * mla::kLkv * 2 : 0);
+  L.lat_pe = take(ctx ? (size_t)cs.max_total * mla::kRope * 2 : 0);
+  L.kn = take((size_t)S * N * P * 2);
+  L.vv = take((size_t)S * N * V * 2);
+  L.o_new = take(ctx ? (size_t)T * N * V * 2 : 0);
+  L.l_new = take(ctx ? (size_t)T * N * 4 : 0);
+  L.o_ctx = take(ctx ? (size_t)T * N * V * 2 : 0);
+  L.l_ctx = take(ctx ? (size_t)T * N * 4 : 0);
+  L.o_chk = take(cs.n > 1 ? (size_t)T * N * V * 2 : 0);
+  L.l_chk = take(cs.n > 1 ? (size_t)T * N * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+int mla_chunked_prefill_workspace_size(const int32_t* new_lens_host, const int32_t* ctx_lens_host, int32_t B,
+                                       int32_t N, int32_t P, int32_t V, int32_t page_size,
+                                       int64_t workspace_tokens, size_t* workspace_bytes_out) {
+  if (!new_lens_host || !ctx_lens_host || !workspace_bytes_out) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || N < 1 || page_size < 1 || workspace_tokens < 1) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  int64_t T = 0;
+  for (int b = 0; b < B; ++b) {
+    if (new_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "negative new-token count");
+    T += new_lens_host[b];
+  }
+  ChunkSched cs;
+  const int rc = chunk_schedule(ctx_lens_host, B, page_size, workspace_tokens, cs);
+  if (rc != MLA_OK) return rc;
+  *workspace_bytes_out = prefill_layout(T, B, N, P, V, cs).total;
+  return MLA_OK;
+}
+
+int mla_chunked_prefill(const void* q_nope, const void* q_pe, const void* kv_c, const void* k_pe,
+                        const int32_t* new_lens_host, const int32_t* ctx_lens_host, int32_t B, const void* cache_kv_c,
+                        const void* cache_k_pe, int64_t cache_s_page, int64_t cache_s_tok, int32_t page_size,
+                        int32_t kv_dtype, float kv_scale, const int32_t* block_table, int64_t block_table_s_req,
+                        const void* W_UK, const void* W_UV, int32_t N, int32_t Lkv, int32_t P, int32_t R,
+                        int32_t V, float scale, int64_t workspace_tokens, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!q_nope || !q_pe || !kv_c || !k_pe || !new_lens_host || !ctx_lens_host || !W_UK || !W_UV || !o)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || N < 1 || page_size < 1 || workspace_tokens < 1) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (Lkv != mla::kLkv || R != mla::kRope || P != 128 || V != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "only Lkv = 512, R = 64, P = 128 and V = 128 are supported");
+  hipStream_t st = (hipStream_t)stream;
+  int64_t T = 0;
+  int32_t max_q = 0;
+  std::vector<int32_t> meta((size_t)B + 1, 0);
+  for (int b = 0; b < B; ++b) {
+    if (new_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "negative new-token count");
+    T += new_lens_host[b];
+    max_q = std::max(max_q, new_lens_host[b]);
+    if (T > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many tokens");
+    meta[b + 1] = (int32_t)T;
+  }
+  ChunkSched cs;
+  int rc = chunk_schedule(ctx_lens_host, B, page_size, workspace_tokens, cs);
+  if (rc != MLA_OK) return rc;
+  if (cs.n > 0 && (!cache_kv_c || !cache_k_pe || !block_table)) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  const PrefillLayout L = prefill_layout(T, B, N, P, V, cs);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace smaller than required (" + std::to_string(L.total) + " bytes)");
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (T == 0) return MLA_OK;
+  for (int i = 0; i < cs.n; ++i) {
+    meta.insert(meta.end(), cs.starts.begin() + (size_t)i * B, cs.starts.begin() + (size_t)(i + 1) * B);
+    meta.insert(meta.end(), cs.cu.begin() + (size_t)i * (B + 1), cs.cu.begin() + (size_t)(i + 1) * (B + 1));
+  }
+  char* ws = (char*)workspace;
+  int32_t* d_meta = (int32_t*)(ws + L.meta);
+  // pageable source: the copy has read it when the call returns
+  hipError_t e = hipMemcpyAsync(d_meta, meta.data(), meta.size() * sizeof(int32_t), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "prefill metadata upload");
+  const int32_t* cu_new = d_meta;
+  void* kn = ws + L.kn;
+  void* vv = ws + L.vv;
+  const bool has_ctx = cs.n > 0;
+
+  // new tokens: up-projection of their own latent rows, causal attention among them
+  rc = mla_kv_b_proj(kv_c, Lkv, W_UK, W_UV, kn, vv, (int32_t)T, N, Lkv, P, V, stream);
+  if (rc != MLA_OK) return rc;
+  void* o_new = has_ctx ? (void*)(ws + L.o_new) : o;
+  float* l_new = has_ctx ? (float*)(ws + L.l_new) : lse;
+  rc = mla_prefill_attention(q_nope, (int64_t)N * P, P, q_pe, (int64_t)N * R, R, kn, (int64_t)N * P, P, k_pe, R, vv,
+                             (int64_t)N * V, V, cu_new, cu_new, B, max_q, N, P, R, V, 1, scale, o_new,
+                             (int64_t)N * V, V, l_new, stream);
+  if (rc != MLA_OK || !has_ctx) return rc;
+
+  // context chunks: gather (and dequantise), up-project, attend without a mask, merge
+  void* lat_kv = ws + L.lat_kv;
+  void* lat_pe = ws + L.lat_pe;
+  void* o_ctx = ws + L.o_ctx;
+  float* l_ctx = (float*)(ws + L.l_ctx);
+  for (int i = 0; i < cs.n; ++i) {
+    const int32_t* d_starts = d_meta + (B + 1) + (size_t)i * (2 * B + 1);
+    const int32_t* d_cu = d_starts + B;
+    const int64_t tot = cs.cu[(size_t)i * (B + 1) + B];
+    rc = mla_gather_context(cache_kv_c, cache_k_pe, cache_s_page, cache_s_tok, page_size, kv_dtype, kv_scale,
+                            block_table, block_table_s_req, d_starts, d_cu, B, tot, lat_kv, mla::kLkv, lat_pe,
+                            mla::kRope, stream);
+    if (rc != MLA_OK) return rc;
+    rc = mla_kv_b_proj(lat_kv, mla::kLkv, W_UK, W_UV, kn, vv, (int32_t)tot, N, Lkv, P, V, stream);
+    if (rc != MLA_OK) return rc;
+    void* oc = i == 0 ? o_ctx : (void*)(ws + L.o_chk);
+    float* lc = i == 0 ? l_ctx : (float*)(ws + L.l_chk);
+    rc = mla_prefill_attention(q_nope, (int64_t)N * P, P, q_pe, (int64_t)N * R, R, kn, (int64_t)N * P, P, lat_pe,
+                               mla::kRope, vv, (int64_t)N * V, V, cu_new, d_cu, B, max_q, N, P, R, V, 0, scale, oc,
+                               (int64_t)N * V, V, lc, stream);
+    if (rc != MLA_OK) return rc;
+    if (i > 0) {
+      rc = merge_attn_states(o_ctx, l_ctx, o_ctx, l_ctx, oc, lc, (int32_t)T, N, V, MLA_DT_BF16, stream);
+      if (rc != MLA_OK) return rc;
+    }
+  }
+  // the context output is the prefix, the new tokens' own output the suffix
+  return merge_attn_states(o, lse, o_ctx, l_ctx, o_new, l_new, (int32_t)T, N, V, MLA_DT_BF16, stream);
 }
 
 }  // extern "C"

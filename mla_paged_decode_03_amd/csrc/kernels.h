@@ -93,4 +93,48 @@ hipError_t launch_gather_rows(const int32_t* block_table, int64_t bt_s, const in
                               const int64_t* offsets, int32_t B, int32_t page_size, int64_t* rows,
                               hipStream_t stream);
 
+// Prefill attention (compute-friendly MLA): per head, q = [q_nope | q_pe] (P+R = 192),
+// k = [k_nope | k_pe] with k_pe shared by all heads, v (V = 128).  Request b owns queries
+// cu_q[b]..cu_q[b+1]-1 and keys cu_k[b]..cu_k[b+1]-1; causal: query i of the request
+// sees keys j <= i + Sk - Sq.  Strides in elements; lse [T, N] (t*N + h) or null.
+struct PrefillAttnArgs {
+  const uint16_t* q_nope;
+  int64_t qn_s_tok, qn_s_head;
+  const uint16_t* q_pe;
+  int64_t qp_s_tok, qp_s_head;
+  const uint16_t* k_nope;
+  int64_t kn_s_tok, kn_s_head;
+  const uint16_t* k_pe;
+  int64_t kp_s_tok;
+  const uint16_t* v;
+  int64_t v_s_tok, v_s_head;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  uint16_t* o;
+  int64_t o_s_tok, o_s_head;
+  float* lse;
+  float scale_log2;  // scale * log2(e)
+  int32_t N, causal;
+};
+// Context gather of one chunk: output row r (request b: cu[b] <= r < cu[b+1]) is
+// context position starts[b] + r - cu[b], as bf16 [kv_c 512] and [k_pe 64] rows.
+struct GatherArgs {
+  const void* kv_c;  // cache base, columns 0..511 (bf16 or e4m3fn)
+  const void* k_pe;  // cache base, columns 512..575
+  int64_t s_page, s_tok;  // elements
+  const int32_t* block_table;
+  int64_t bt_s;
+  const int32_t* starts;  // [B]
+  const int32_t* cu;      // [B + 1]
+  uint16_t* out_kv_c;
+  int64_t okv_s;
+  uint16_t* out_k_pe;
+  int64_t ope_s;
+  float kv_scale;
+  int64_t total;
+  int32_t B, page_size;
+};
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, int32_t B, int32_t max_q, hipStream_t stream);
+hipError_t launch_gather_ctx(const GatherArgs& a, bool fp8, hipStream_t stream);
+
 }  // namespace mla

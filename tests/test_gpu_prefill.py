@@ -1,0 +1,216 @@
+"""GPU parity of the chunked-prefill path (compute-friendly form) against the oracle.
+
+Pieces: the per-head attention kernel (causal and unmasked, ragged requests, empty
+requests and key sets), the context gather (bf16 bit-exact, fp8 within one bf16
+rounding of the dequantised value), kv_b_proj, and the whole chunked prefill (several
+chunks, requests without context, bf16 and fp8 caches) against the oracle's definition
+of the output, with the pipeline's intermediate tensors (dequantised context rows,
+k_nope, v) rounded to bf16 as the pages hold them.  Tolerances: the bf16 output bounds of
+the decode path (max-abs 1e-2, rel-L2 5e-3) and 1e-3 on the LSE.
+"""
+import numpy as np
+import pytest
+
+from tests._lib import LSE_MAX_ABS, O_MAX_ABS, O_REL_L2, bf16_dev, bf16_host, ensure_built, metrics, u8_dev
+
+pytestmark = pytest.mark.gpu
+ensure_built()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests selected but no GPU is visible")
+    return torch
+
+
+def _bf16(rng, shape, s=1.0):
+    from mla_paged_decode_03_amd.inputs import f32_to_bf16_bits
+    return f32_to_bf16_bits((rng.standard_normal(shape) * s).astype(np.float32))
+
+
+def _check(o, lse, ro, rl, where=""):
+    valid = np.isfinite(rl)
+    mx, rel = metrics(o, ro)
+    dl = np.abs(np.where(valid, lse, 0) - np.where(valid, rl, 0))
+    print(where, "max_abs", mx, "rel_l2", rel, "lse", float(dl.max()) if dl.size else 0.0,
+          np.unravel_index(np.argmax(dl), dl.shape) if dl.size else None,
+          "finite mismatch", int((np.isfinite(lse) != valid).sum()), flush=True)
+    assert mx <= O_MAX_ABS and rel <= O_REL_L2, (where, mx, rel)
+    assert np.array_equal(np.isfinite(lse), valid), where
+    if valid.any():
+        assert np.max(np.abs(lse[valid] - rl[valid])) <= LSE_MAX_ABS, where
+    assert np.all(o[~valid] == 0), where
+
+
+@pytest.mark.parametrize("causal,sq,sk", [
+    (True, [37, 130, 1, 0, 256], [87, 330, 1, 5, 256]),
+    (False, [37, 130, 1, 3, 64], [50, 0, 7, 300, 33]),
+])
+def test_prefill_attention(torch_cuda, causal, sq, sk):
+    torch = torch_cuda
+    from mla_paged_decode_03_amd import api
+    from oracle import prefill as PF
+    from oracle.formats import bf16_to_f64
+    rng = np.random.default_rng(31 + causal)
+    N, P, R, V = 5, 128, 64, 128
+    cq = np.concatenate([[0], np.cumsum(sq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(sk)]).astype(np.int32)
+    T, S = int(cq[-1]), int(ck[-1])
+    qn, qp = _bf16(rng, (T, N, P)), _bf16(rng, (T, N, R))
+    kn, kp, v = _bf16(rng, (S, N, P)), _bf16(rng, (S, R)), _bf16(rng, (S, N, V))
+    scale = 1.0 / np.sqrt(P + R)
+    o = torch.full((T, N, V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+    api.mla_prefill_attention(bf16_dev(qn), bf16_dev(qp), bf16_dev(kn), bf16_dev(kp), bf16_dev(v),
+                              torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda(), max(sq), causal,
+                              scale, o, lse)
+    torch.cuda.synchronize()
+    go, gl = bf16_host(o), lse.cpu().numpy()
+    for b in range(len(sq)):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 == q0:
+            continue
+        ro, rl = PF.mha(bf16_to_f64(qn[q0:q1]), bf16_to_f64(qp[q0:q1]), bf16_to_f64(kn[k0:k1]),
+                        bf16_to_f64(kp[k0:k1]), bf16_to_f64(v[k0:k1]), scale, causal)
+        _check(go[q0:q1], gl[q0:q1], ro, rl, f"request {b}")
+
+
+def test_prefill_attention_dominant_key_exact(torch_cuda):
+    """A key whose logit leads every other by far takes all the weight: o equals its
+    value row bitwise, in every tile position of the causal window."""
+    torch = torch_cuda
+    from mla_paged_decode_03_amd import api
+    from mla_paged_decode_03_amd.inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(7)
+    N, P, R, V, S = 2, 128, 64, 128, 70
+    qn = np.zeros((S, N, P), np.uint16)
+    kn = np.zeros((S, N, P), np.uint16)
+    v = _bf16(rng, (S, N, V))
+    # query i points at key (i * 7) % (i + 1), through the rope part only
+    kp_f = np.zeros((S, R), np.float32)
+    qp_f = np.zeros((S, N, R), np.float32)
+    target = np.array([(i * 7) % (i + 1) for i in range(S)])
+    for j in range(S):
+        kp_f[j, j % R] = 1.0
+    for i in range(S):
+        qp_f[i, :, target[i] % R] = 3000.0
+    # queries whose window holds another key on the target's rope slot would tie: skipped
+    ok = np.array([all(j == target[i] or j % R != target[i] % R for j in range(i + 1)) for i in range(S)])
+    cq = torch.tensor([0, S], dtype=torch.int32, device="cuda")
+    o = torch.empty((S, N, V), dtype=torch.bfloat16, device="cuda")
+    api.mla_prefill_attention(bf16_dev(qn), bf16_dev(f32_to_bf16_bits(qp_f)), bf16_dev(kn),
+                              bf16_dev(f32_to_bf16_bits(kp_f)), bf16_dev(v), cq, cq, S, True, 1.0, o)
+    torch.cuda.synchronize()
+    got = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    for i in np.nonzero(ok)[0]:
+        assert np.array_equal(got[i], v[target[i]]), i
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_gather_context(torch_cuda, kv_dtype):
+    torch = torch_cuda
+    from mla_paged_decode_03_amd import api
+    from mla_paged_decode_03_amd import inputs as gen
+    from oracle import prefill as PF
+    ctx = np.array([100, 0, 257, 16], np.int32)
+    w = gen.workload("tiny", B=4, N=1, page_size=16, pool_pages=None, kv_dtype=kv_dtype, seed=41)
+    inp = gen.generate(w, seq_lens=ctx)
+    mcc, starts, lens, cu = PF.chunk_plan(ctx, 96, 16)
+    cache = u8_dev(inp.cache) if kv_dtype == "fp8" else bf16_dev(inp.cache)
+    bt = torch.from_numpy(inp.block_table).cuda()
+    for i in range(len(starts)):
+        tot = int(cu[i, -1])
+        okv = torch.empty((max(tot, 1), 512), dtype=torch.bfloat16, device="cuda")
+        ope = torch.empty((max(tot, 1), 64), dtype=torch.bfloat16, device="cuda")
+        api.mla_gather_context(cache, bt, torch.from_numpy(starts[i].astype(np.int32)).cuda(),
+                               torch.from_numpy(cu[i].astype(np.int32)).cuda(), tot, okv, ope,
+                               kv_scale=inp.kv_scale)
+        torch.cuda.synchronize()
+        got = np.concatenate([bf16_host(okv), bf16_host(ope)], axis=1)[:tot]
+        ref = np.concatenate([PF.context_rows(inp.cache, kv_dtype, inp.kv_scale, inp.block_table, b,
+                                              int(starts[i, b]), int(lens[i, b])) for b in range(len(ctx))])
+        if kv_dtype == "bf16":
+            assert np.array_equal(got, ref)
+        else:  # one rounding of the dequantised value to bf16
+            assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref))
+
+
+def test_kv_b_proj(torch_cuda):
+    torch = torch_cuda
+    from mla_paged_decode_03_amd import api
+    from oracle import prefill as PF
+    from oracle.formats import bf16_to_f64
+    rng = np.random.default_rng(43)
+    S, N, P, V = 300, 3, 128, 128
+    kv = _bf16(rng, (S, 512))
+    wk, wv = _bf16(rng, (512, N, P), 0.02), _bf16(rng, (512, N, V), 0.02)
+    kn = torch.empty((S, N, P), dtype=torch.bfloat16, device="cuda")
+    vv = torch.empty((S, N, V), dtype=torch.bfloat16, device="cuda")
+    api.mla_kv_b_proj(bf16_dev(kv), bf16_dev(wk), bf16_dev(wv), kn, vv)
+    torch.cuda.synchronize()
+    rk, rv = PF.kv_b_proj(bf16_to_f64(kv), bf16_to_f64(wk), bf16_to_f64(wv))
+    for got, ref in ((bf16_host(kn), rk), (bf16_host(vv), rv)):
+        mx, rel = metrics(got, ref)
+        assert mx <= O_MAX_ABS and rel <= O_REL_L2, (mx, rel)
+        # fp32 accumulation, one rounding: within one bf16 step of the exact value
+        assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-6)
+
+
+def _oracle_prefill(inp, requests=None):
+    from oracle import prefill as PF
+    from oracle.formats import bf16_to_f64
+    return PF.chunked_prefill(
+        bf16_to_f64(inp.q_nope), bf16_to_f64(inp.q_pe), inp.cu_new, bf16_to_f64(inp.kv_c), bf16_to_f64(inp.k_pe),
+        inp.ctx.seq_lens, inp.ctx.cache, inp.ctx.w.kv_dtype, inp.ctx.kv_scale, inp.ctx.block_table,
+        bf16_to_f64(inp.W_UK), bf16_to_f64(inp.W_UV), inp.scale, requests=requests, kv_round="bf16")
+
+
+def run_prefill(torch, inp, workspace_tokens, with_lse=True):
+    from mla_paged_decode_03_amd import api
+    T, N = inp.T, inp.N
+    cache = u8_dev(inp.ctx.cache) if inp.ctx.w.kv_dtype == "fp8" else bf16_dev(inp.ctx.cache)
+    ws_bytes = api.mla_chunked_prefill_workspace_size(inp.new_lens, inp.ctx.seq_lens, N, inp.P, inp.V,
+                                                     inp.ctx.w.page_size, workspace_tokens)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    o = torch.full((T, N, inp.V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
+    api.mla_chunked_prefill(bf16_dev(inp.q_nope), bf16_dev(inp.q_pe), bf16_dev(inp.kv_c), bf16_dev(inp.k_pe),
+                            inp.new_lens, inp.ctx.seq_lens, cache, torch.from_numpy(inp.ctx.block_table).cuda(),
+                            bf16_dev(inp.W_UK), bf16_dev(inp.W_UV), inp.scale, workspace_tokens, o, lse, ws,
+                            kv_scale=inp.ctx.kv_scale)
+    torch.cuda.synchronize()
+    return bf16_host(o), (lse.cpu().numpy() if with_lse else None)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("ctx,new,wt", [
+    ([100, 0, 257], [20, 33, 1], 96),      # 6 chunks of 48, a request without context
+    ([0, 0], [5, 140], 64),               # no context at all: one causal pass
+    ([64, 640], [130, 7], 4096),          # one chunk
+])
+def test_chunked_prefill(torch_cuda, kv_dtype, ctx, new, wt):
+    from mla_paged_decode_03_amd import inputs as gen
+    inp = gen.generate_prefill(ctx, new, N=8, page_size=16, kv_dtype=kv_dtype, seed=2100 + len(ctx))
+    o, lse = run_prefill(torch_cuda, inp, wt)
+    ro, rl = _oracle_prefill(inp)
+    _check(o, lse, ro, rl, f"{kv_dtype} ctx={ctx} new={new}")
+
+
+def test_chunked_prefill_workspace_errors(torch_cuda):
+    from mla_paged_decode_03_amd import api
+    with pytest.raises(api.MLAError) as e:
+        api.mla_chunked_prefill_workspace_size([1, 1, 1], [5, 5, 5], 8, 128, 128, 16, 2)
+    assert e.value.status == api.MLA_ERR_WORKSPACE
+    from mla_paged_decode_03_amd import inputs as gen
+    inp = gen.generate_prefill([40], [3], N=2, page_size=16, seed=5)
+    torch = torch_cuda
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    o = torch.empty((3, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(api.MLAError) as e:
+        api.mla_chunked_prefill(bf16_dev(inp.q_nope), bf16_dev(inp.q_pe), bf16_dev(inp.kv_c), bf16_dev(inp.k_pe),
+                                inp.new_lens, inp.ctx.seq_lens, bf16_dev(inp.ctx.cache),
+                                torch.from_numpy(inp.ctx.block_table).cuda(), bf16_dev(inp.W_UK),
+                                bf16_dev(inp.W_UV), inp.scale, 32, o, None, ws)
+    assert e.value.status == api.MLA_ERR_WORKSPACE
