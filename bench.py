@@ -12,6 +12,7 @@ dominant kernel (the decode kernel, timed with HIP events on the stream it is
 launched on) and the CPU fp64 oracle timed on a bounded sample of the same batch.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3|longtail|verify|fp8|tiny]
+  python bench.py --workload prefill   # chunked prefill (compute-friendly form), DSV3 heads
   python bench.py --calibrate-copy     # a plain device copy of known size, for counter scaling
 
 roofline.traffic is the decode kernel's HBM bytes per launch from rocprofv3 FETCH_SIZE and
@@ -166,6 +167,170 @@ def cpu_baseline(inp, o_gpu, budget_s, q_scale=None):
     return base, dict(requests=len(errs), max_abs=max_abs, rel_l2=rel_l2)
 
 
+PREFILL_METRIC = "MLA chunked-prefill tokens/s and MFMA TFLOP/s (% roofline), DSV3 heads"
+
+
+def prefill_work(ctx_lens, new_lens, N, P, R, V, mcc):
+    """Flops of a chunked-prefill step: kv_b_proj of every context and new token, the new
+    tokens' causal attention and their attention to every context chunk."""
+    C = np.asarray(ctx_lens, np.int64)
+    S = np.asarray(new_lens, np.int64)
+    per_pair = 2 * N * (P + R + V)
+    causal_pairs = int((S * (S + 1) // 2).sum())
+    ctx_pairs = int((S * C).sum())
+    gemm = 2 * int((C + S).sum()) * LKV * N * (P + V)
+    # the dominant launch: one context chunk (every request with mcc context keys)
+    chunk_pairs = int((S * np.minimum(C, mcc)).sum())
+    return dict(attn_flops=per_pair * (causal_pairs + ctx_pairs), gemm_flops=gemm,
+                chunk_attn_flops=per_pair * chunk_pairs, causal_pairs=causal_pairs, ctx_pairs=ctx_pairs)
+
+
+def bench_prefill(args):
+    import torch
+    from mla_paged_decode_03_amd import api
+    from mla_paged_decode_03_amd import inputs as gen
+    cfg = dict(gen.PREFILL_WORKLOAD)
+    wt = cfg.pop("workspace_tokens")
+    t_gen = time.perf_counter()
+    inp = gen.generate_prefill(**cfg)
+    t_gen = time.perf_counter() - t_gen
+    dev = "cuda"
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    T, N, P, V = inp.T, inp.N, inp.P, inp.V
+    ctx_lens, new_lens = inp.ctx.seq_lens, inp.new_lens
+    q_nope, q_pe, kv_c, k_pe = bf16(inp.q_nope), bf16(inp.q_pe), bf16(inp.kv_c), bf16(inp.k_pe)
+    W_UK, W_UV = bf16(inp.W_UK), bf16(inp.W_UV)
+    cache = bf16(inp.ctx.cache) if inp.ctx.w.kv_dtype == "bf16" else \
+        torch.from_numpy(inp.ctx.cache).view(torch.float8_e4m3fn).to(dev)
+    bt = torch.from_numpy(inp.ctx.block_table).to(dev)
+    ws_bytes = api.mla_chunked_prefill_workspace_size(new_lens, ctx_lens, N, P, V, inp.ctx.w.page_size, wt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty((T, N, V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, N), dtype=torch.float32, device=dev)
+
+    def step():
+        api.mla_chunked_prefill(q_nope, q_pe, kv_c, k_pe, new_lens, ctx_lens, cache, bt, W_UK, W_UV, inp.scale,
+                                wt, o, lse, ws, kv_scale=inp.ctx.kv_scale)
+
+    for _ in range(args.warmup):
+        step()
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / K * 1e3
+
+    # The dominant kernel: the attention of all new tokens against one context chunk
+    # (mcc keys per request), timed as back-to-back launches on the launch stream.
+    with_ctx = int((ctx_lens > 0).sum())
+    mcc = wt // max(with_ctx, 1)
+    mcc = mcc // inp.ctx.w.page_size * inp.ctx.w.page_size if mcc >= inp.ctx.w.page_size else mcc
+    ck = np.concatenate([[0], np.cumsum(np.minimum(ctx_lens, mcc))]).astype(np.int32)
+    S = int(ck[-1])
+    g = torch.Generator(device=dev).manual_seed(7)
+    kn = (torch.randn((S, N, P), device=dev, generator=g) * 0.45).to(torch.bfloat16)
+    vv = (torch.randn((S, N, V), device=dev, generator=g) * 0.45).to(torch.bfloat16)
+    kp = torch.randn((S, ROPE), device=dev, generator=g).to(torch.bfloat16)
+    cq_t = torch.from_numpy(inp.cu_new.astype(np.int32)).to(dev)
+    ck_t = torch.from_numpy(ck).to(dev)
+    oc = torch.empty_like(o)
+    lc = torch.empty_like(lse)
+    max_q = int(new_lens.max())
+
+    def attn():
+        api.mla_prefill_attention(q_nope, q_pe, kn, kp, vv, cq_t, ck_t, max_q, False, inp.scale, oc, lc)
+
+    def gemm():
+        api.mla_kv_b_proj(kv_c, W_UK, W_UV, kn[:T], vv[:T])
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+    reps = max(3, min(K, 20))
+    attn_us = timed(attn, reps)
+    gemm_us = timed(gemm, reps)
+
+    work = prefill_work(ctx_lens, new_lens, N, P, ROPE, V, mcc)
+    attn_tflops = work["chunk_attn_flops"] / (attn_us * 1e-6) / 1e12
+    gemm_tflops = 2 * T * LKV * N * (P + V) / (gemm_us * 1e-6) / 1e12
+    step_tflops = (work["attn_flops"] + work["gemm_flops"]) / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": PREFILL_METRIC, "value": round(T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill", "B": int(len(ctx_lens)), "N": N, "P": P, "R": ROPE, "V": V, "Lkv": LKV,
+                   "ctx_lens": [int(x) for x in ctx_lens], "new_lens": [int(x) for x in new_lens],
+                   "page_size": inp.ctx.w.page_size, "kv_dtype": inp.ctx.w.kv_dtype, "workspace_tokens": wt,
+                   "chunk_tokens": int(mcc)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "attn_chunk_kernel_us": round(attn_us, 1), "kv_b_proj_us": round(gemm_us, 1),
+        "kv_b_proj_tflops": round(gemm_tflops, 1), "step_tflops": round(step_tflops, 1),
+        "frac_step_mfma": round(step_tflops / BF16_PEAK_TFLOPS, 4), "algorithmic": work,
+        "input_gen_s": round(t_gen, 2),
+    }
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        line["cpu_baseline"], line["parity_sample"] = prefill_cpu_baseline(inp, bf16_host_np(o), args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+def bf16_host_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def prefill_cpu_baseline(inp, o_gpu, budget_s):
+    """The fp64 oracle, as it stands, on (request, head) pairs of the batch in order until
+    budget_s seconds are used: each pair is the whole chunked-prefill output of that head
+    for the request's new tokens (heads are independent, so the oracle is given that
+    head's slice of the weights and queries).  tokens/s counts query tokens x heads / N."""
+    from oracle import prefill as PF
+    from oracle.formats import bf16_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        cores = int(os.environ["OMP_NUM_THREADS"])
+    N = inp.N
+    B = len(inp.new_lens)
+    qn, qp = bf16_to_f64(inp.q_nope), bf16_to_f64(inp.q_pe)
+    kv, kpe = bf16_to_f64(inp.kv_c), bf16_to_f64(inp.k_pe)
+    WK, WV = bf16_to_f64(inp.W_UK), bf16_to_f64(inp.W_UV)
+    pairs = [(b, h) for h in range(N) for b in range(B)]
+    t_used, done, errs = 0.0, [], []
+    for b, h in pairs:
+        lo, hi = int(inp.cu_new[b]), int(inp.cu_new[b + 1])
+        t0 = time.perf_counter()
+        ro, _ = PF.chunked_prefill(qn[:, h:h + 1], qp[:, h:h + 1], inp.cu_new, kv, kpe, inp.ctx.seq_lens,
+                                   inp.ctx.cache, inp.ctx.w.kv_dtype, inp.ctx.kv_scale, inp.ctx.block_table,
+                                   WK[:, h:h + 1], WV[:, h:h + 1], inp.scale, requests=[b], kv_round="bf16")
+        t_used += time.perf_counter() - t0
+        done.append((b, h, hi - lo))
+        d = o_gpu[lo:hi, h] - ro[lo:hi, 0]
+        errs.append((float(np.max(np.abs(d))), float(np.sum(d * d)), float(np.sum(ro[lo:hi, 0] ** 2))))
+        if t_used >= budget_s:
+            break
+    head_toks = sum(x[2] for x in done)
+    base = dict(value=head_toks / N / t_used, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{len(done)} (request, head) pairs of the {B}x{N} batch ({head_toks} query-token heads, "
+                       f"each over its request's full context), {t_used:.1f} s of fp64 numpy")
+    parity = dict(pairs=len(errs), max_abs=max(e[0] for e in errs),
+                  rel_l2=float(np.sqrt(sum(e[1] for e in errs) / max(sum(e[2] for e in errs), 1e-300))))
+    return base, parity
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +352,10 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(max(1, min(args.steps, 5)))
+        return
+
+    if args.workload == "prefill":
+        bench_prefill(args)
         return
 
     import torch
