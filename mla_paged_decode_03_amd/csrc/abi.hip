@@ -560,10 +560,12 @@ int mla_prefill_attention(const void* q_nope, int64_t q_nope_s_tok, int64_t q_no
                           void* o, int64_t o_s_tok, int64_t o_s_head, float* lse, void* stream) {
   if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !cu_q || !cu_k || !o)
     return fail(MLA_ERR_INVALID_ARG, "null pointer");
-  if (B < 0 || B > 65535 || max_q < 0 || N < 1 || N > 65535) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (B < 0 || max_q < 0 || N < 1) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if ((int64_t)((max_q + 127) / 128) * N * B > (int64_t)INT32_MAX - 8)
+    return fail(MLA_ERR_UNSUPPORTED, "too many (request, head, query block) items");
   if (P != 128 || R != mla::kRope || V != 128)
     return fail(MLA_ERR_UNSUPPORTED, "only P = 128, R = 64 and V = 128 are supported");
-  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (q_nope_s_head < P || q_pe_s_head < R || k_nope_s_head < P || v_s_head < V || o_s_head < V ||
       q_nope_s_tok < (int64_t)N * q_nope_s_head || q_pe_s_tok < (int64_t)N * q_pe_s_head ||
       k_nope_s_tok < (int64_t)N * k_nope_s_head || k_pe_s_tok < R || v_s_tok < (int64_t)N * v_s_head ||

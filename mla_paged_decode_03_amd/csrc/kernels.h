@@ -115,6 +115,7 @@ struct PrefillAttnArgs {
   float* lse;
   float scale_log2;  // scale * log2(e)
   int32_t N, causal;
+  int32_t q_blocks, items, per_xcd;  // set by the launcher
 };
 // Context gather of one chunk: output row r (request b: cu[b] <= r < cu[b+1]) is
 // context position starts[b] + r - cu[b], as bf16 [kv_c 512] and [k_pe 64] rows.

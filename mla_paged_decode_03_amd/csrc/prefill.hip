@@ -9,12 +9,15 @@
 // a mask, and the chunk outputs are merged by LSE; the new tokens attend to themselves
 // causally, and one last merge combines the two.
 //
-// Attention kernel.  One workgroup (4 waves) per (request, block of 128 queries, head);
-// wave w owns queries 32w..32w+31, one per lane column.  Per tile of 32 keys:
+// Attention kernel.  One workgroup (4 waves, one per SIMD) per (request, block of 256
+// queries, head); wave w owns queries 64w..64w+63 as two blocks of 32, one query per lane
+// column in each.  Per tile of 32 keys and per query block:
 //   S^T[key][query] = K[key][:] . Q[query][:]     (12 MFMAs 32x32x16, K from LDS)
 //   online softmax per query (the 16 logits of a lane plus its partner lane l^32)
 //   O^T[v][query]  += V^T[v][key] . P^T[key][query] (8 MFMAs, V^T from LDS)
 // so every per-query quantity (maximum, row sum, rescale factor) is a per-lane scalar.
+// Each K and V^T fragment read from LDS feeds the MFMAs of both query blocks: at one
+// block per wave the LDS reads alone (1 KB per MFMA per wave) would match the MFMA rate.
 // K sits in LDS as [key][192] rows of 400 bytes and V transposed as [v][32 keys] rows of
 // 72 bytes: both strides make the 16-lane (b128) and 32-lane (b64) reads of one MFMA
 // operand hit distinct banks.  The next tile is loaded into registers while the current
@@ -33,11 +36,21 @@ constexpr int kPN = 128;         // P (k_nope / q_nope width)
 constexpr int kPR = 64;          // R (rope width)
 constexpr int kPV = 128;         // V (value width)
 
+constexpr float kRescaleAt = 8.f;  // log2 units a tile maximum may exceed the reference by
+
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[kPT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t sv[kPV * kVRow];
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int qb = gridDim.x - 1 - blockIdx.x;  // longest (causal) blocks first
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by launch index, so
+  // launch index L takes work item (L % 8) * per + L / 8.  Each XCD then runs a contiguous
+  // range of (request, head, query block) items: the query blocks of one head share that
+  // XCD's L2 for their K and V tiles instead of each XCD streaming every head.
+  const int L = blockIdx.x;
+  const int item = (L & 7) * a.per_xcd + (L >> 3);
+  if (item >= a.items) return;  // (whole workgroup; the launch is padded to 8 * per_xcd)
+  const int nqb = a.q_blocks;
+  const int qb = nqb - 1 - item % nqb;  // longest (causal) blocks first
+  const int h = (item / nqb) % a.N, b = item / nqb / a.N;
   const int q0 = a.cu_q[b], Sq = a.cu_q[b + 1] - q0;
   const int k0 = a.cu_k[b], Sk = a.cu_k[b + 1] - k0;
   if (128 * qb >= Sq) return;  // (whole workgroup)
@@ -49,6 +62,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   const int nkeys = a.causal ? max(0, min(Sk, qlast + Sk - Sq + 1)) : Sk;
   const int ntiles = (nkeys + kPT - 1) / kPT;
   const int qlim = a.causal ? qi + Sk - Sq : Sk - 1;  // last key this lane's query sees
+  // tiles below this key count need no mask for any query of the workgroup
+  const int unmasked = a.causal ? max(0, min(Sk, 128 * qb + Sk - Sq + 1)) : Sk;
 
   // queries: k-step ks covers dims 16 ks + 8 hh .. +7 (q_nope for ks < 8, q_pe after)
   u32x4_t qf[12];
@@ -63,45 +78,48 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     }
   }
 
-  // tile loads: K as 32 keys x 24 chunks of 16 B (3 per thread); V by threads 0..127 as
-  // 4 keys x 8 values each (transposed on the way to LDS)
+  // Tile loads.  K: thread t covers key t / 8 of the tile, chunks 3 (t % 8) .. +2 of its
+  // 24 (16 of k_nope, 8 of k_pe).  V: threads 0..127 cover 4 keys x 8 values each, which
+  // are transposed on the way to LDS.  Row pointers advance by one tile per load.
+  const int kkey = tid >> 3, kc0 = 3 * (tid & 7);
+  const uint16_t* pn = a.k_nope + ((int64_t)k0 + kkey) * a.kn_s_tok + (int64_t)h * a.kn_s_head;
+  const uint16_t* pp = a.k_pe + ((int64_t)k0 + kkey) * a.kp_s_tok;
+  const int vq = (tid >> 4) & 7, vo = tid & 15;
+  const uint16_t* pv = a.v + ((int64_t)k0 + 4 * vq) * a.v_s_tok + (int64_t)h * a.v_s_head + 8 * vo;
+  const int64_t step_n = (int64_t)kPT * a.kn_s_tok, step_p = (int64_t)kPT * a.kp_s_tok;
+  const int64_t step_v = (int64_t)kPT * a.v_s_tok;
   u32x4_t rk[3], rv[4];
   auto load = [&](int kt) __attribute__((always_inline)) {
+    const bool full = kt * kPT + kPT <= Sk;  // (uniform) every key of the tile exists
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int u = tid + 256 * i, key = u / 24, c = u - 24 * key;
-      const int j = kt * kPT + key;
+      const int c = kc0 + i;
       rk[i] = u32x4_t{0, 0, 0, 0};
-      if (j < Sk) {
-        const int64_t s = (int64_t)k0 + j;
-        rk[i] = c < 16 ? *(const u32x4_t*)(a.k_nope + s * a.kn_s_tok + (int64_t)h * a.kn_s_head + 8 * c)
-                       : *(const u32x4_t*)(a.k_pe + s * a.kp_s_tok + 8 * (c - 16));
-      }
+      if (full || kt * kPT + kkey < Sk) rk[i] = c < 16 ? *(const u32x4_t*)(pn + 8 * c) : *(const u32x4_t*)(pp + 8 * (c - 16));
     }
     if (tid < 128) {
-      const int kq = tid >> 4, vo = tid & 15;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = kt * kPT + 4 * kq + r;
         rv[r] = u32x4_t{0, 0, 0, 0};
-        if (j < Sk) rv[r] = *(const u32x4_t*)(a.v + ((int64_t)k0 + j) * a.v_s_tok + (int64_t)h * a.v_s_head + 8 * vo);
+        if (full || kt * kPT + 4 * vq + r < Sk) rv[r] = *(const u32x4_t*)(pv + r * a.v_s_tok);
       }
     }
+    pn += step_n;
+    pp += step_p;
+    pv += step_v;
   };
   auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int u = tid + 256 * i, key = u / 24, c = u - 24 * key;
-      *(u32x4_t*)(sk + key * kKRow + 8 * c) = rk[i];
-    }
+    for (int i = 0; i < 3; ++i) *(u32x4_t*)(sk + kkey * kKRow + 8 * (kc0 + i)) = rk[i];
     if (tid < 128) {
-      const int kq = tid >> 4, vo = tid & 15;
+      // value c of keys 4vq .. 4vq+3 -> V^T row 8vo + c: the 16-bit halves of two dwords
+      // joined by one byte permute each
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const int sh = 16 * (c & 1);
-        const uint32_t e0 = (rv[0][c >> 1] >> sh) & 0xFFFFu, e1 = (rv[1][c >> 1] >> sh) & 0xFFFFu;
-        const uint32_t e2 = (rv[2][c >> 1] >> sh) & 0xFFFFu, e3 = (rv[3][c >> 1] >> sh) & 0xFFFFu;
-        *(u32x2_t*)(sv + (8 * vo + c) * kVRow + 4 * kq) = u32x2_t{e0 | (e1 << 16), e2 | (e3 << 16)};
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t w01 = __builtin_amdgcn_perm(rv[1][c >> 1], rv[0][c >> 1], sel);
+        const uint32_t w23 = __builtin_amdgcn_perm(rv[3][c >> 1], rv[2][c >> 1], sel);
+        *(u32x2_t*)(sv + (8 * vo + c) * kVRow + 4 * vq) = u32x2_t{w01, w23};
       }
     }
   };
@@ -111,67 +129,82 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[vb][e] = 0.f;
-  float m = -INFINITY, lsum = 0.f;  // log2-domain running maximum; this half's row sum
+  // Softmax state in log2 units: p = 2^(c s - m) against a reference maximum m that only
+  // moves when a logit exceeds it by more than kRescaleAt (p then stays below 2^8), so O
+  // is rescaled rarely; lsum is this half's row sum.
+  float m = -INFINITY, lsum = 0.f;
+  const float cs = a.scale_log2;
 
-  if (ntiles > 0) load(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();  // the previous tile's reads are done
-    store();
-    __syncthreads();
-    if (kt + 1 < ntiles) load(kt + 1);  // in flight during this tile's math
-
+  auto tile = [&](int kt) __attribute__((always_inline)) {
+    // all K fragments of the tile are read before the MFMA chain starts, so that no MFMA
+    // waits for an LDS round trip
+    u32x4_t kf[12];
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) kf[ks] = *(const u32x4_t*)(sk + l32 * kKRow + 16 * ks + 8 * hh);
     f32x16_t s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) {
-      const u32x4_t kf = *(const u32x4_t*)(sk + l32 * kKRow + 16 * ks + 8 * hh);
-      s = mfma32(kf, qf[ks], s);
+    for (int ks = 0; ks < 12; ++ks) s = mfma32(kf[ks], qf[ks], s);
+    u32x4_t vf[8];  // V^T fragments, read while the softmax runs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t* vr = sv + (32 * (i >> 1) + l32) * kVRow + 16 * (i & 1) + 4 * hh;
+      const u32x2_t lo = *(const u32x2_t*)vr, hi = *(const u32x2_t*)(vr + 8);
+      vf[i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     }
     // lane holds keys 8 gq + 4 hh + e of the tile (index 4 gq + e) for query qi
+    if (kt * kPT + kPT > unmasked) {  // (uniform) a tile on the diagonal or past Sk
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        const int j = kt * kPT + 8 * (idx >> 2) + 4 * hh + (idx & 3);
+        if (j > qlim || j >= Sk) s[idx] = -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, s[idx]);
+    mx = half_max(mx) * cs;  // scale > 0: the maximum of the scaled logits
+    if (__any(mx > m + kRescaleAt)) {
+      const float m_new = mx > m + kRescaleAt ? mx : m;
+      const float alpha = m_new == m ? 1.f : exp2f(m - m_new);  // 0 while m is -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[vb][e] *= alpha;
+      m = m_new;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;  // a row with no key yet: every p is 0
     float x[16];
-    float mx = -INFINITY;
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
-      const int j = kt * kPT + 8 * (idx >> 2) + 4 * hh + (idx & 3);
-      x[idx] = (j <= qlim && j < Sk) ? s[idx] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[idx]);
+      x[idx] = exp2f(fmaf(s[idx], cs, -m_use));
+      lsum += x[idx];
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);  // 0 while m is -inf
-    float ps = 0.f;
-#pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      x[idx] = exp2f(x[idx] - m_use);
-      ps += x[idx];
-    }
-    lsum = lsum * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[vb][e] *= alpha;
-    // P^T operand of k-step ss: k-slot 8 hh + c <-> key 16 ss + 4 hh + c (c < 4) and
-    // 16 ss + 8 + 4 hh + (c - 4) (c >= 4): accumulator indices 8 ss .. 8 ss + 7
+    // P^T operand of k-step ss: k-slot 8 hh + i <-> key 16 ss + 4 hh + i (i < 4) and
+    // 16 ss + 8 + 4 hh + (i - 4) (i >= 4): accumulator indices 8 ss .. 8 ss + 7
     u32x4_t pb[2];
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss)
       pb[ss] = u32x4_t{pack_bf16x2(x[8 * ss], x[8 * ss + 1]), pack_bf16x2(x[8 * ss + 2], x[8 * ss + 3]),
                        pack_bf16x2(x[8 * ss + 4], x[8 * ss + 5]), pack_bf16x2(x[8 * ss + 6], x[8 * ss + 7])};
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const uint16_t* vr = sv + (32 * vb + l32) * kVRow + 16 * ss + 4 * hh;
-        const u32x2_t lo = *(const u32x2_t*)vr, hi = *(const u32x2_t*)(vr + 8);
-        o[vb] = mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[ss], o[vb]);
-      }
+    for (int i = 0; i < 8; ++i) o[i >> 1] = mfma32(vf[i], pb[i & 1], o[i >> 1]);
+  };
+
+  // the next tile is in registers while this one is stored and computed
+  if (ntiles > 0) load(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    __syncthreads();  // the previous tile's reads are done
+    store();
+    __syncthreads();
+    if (kt + 1 < ntiles) load(kt + 1);
+    tile(kt);
   }
 
   // epilogue: o = O / l (bf16), lse = ln sum exp (scale included); no key -> 0, -inf
-  const float lrow = lsum + __shfl_xor(lsum, 32);
+  const float lrow = half_sum(lsum);
   if (!qvalid) return;
   const int64_t t = (int64_t)q0 + qi;
   const float f = lrow > 0.f ? 1.f / lrow : 0.f;
@@ -235,8 +268,11 @@ __global__ __launch_bounds__(256) void gather_ctx_kernel(GatherArgs a) {
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, int32_t B, int32_t max_q, hipStream_t stream) {
   if (B == 0 || max_q == 0) return hipSuccess;
-  const dim3 grid((max_q + 127) / 128, a.N, B);
-  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(256), 0, stream, a);
+  PrefillAttnArgs g = a;
+  g.q_blocks = (max_q + 127) / 128;
+  g.items = g.q_blocks * a.N * B;
+  g.per_xcd = (g.items + 7) / 8;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(8 * g.per_xcd), dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
