@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     mx = half_max(mx) * cs;  // scale > 0: the maximum of the scaled logits
     if (__any(mx > m + kRescaleAt)) {
       const float m_new = mx > m + kRescaleAt ? mx : m;
-      const float alpha = m_new == m ? 1.f : exp2f(m - m_new);  // 0 while m is -inf
+      const float alpha = m_new == m ? 1.f : fast_exp2(m - m_new);  // 0 while m is -inf
       lsum *= alpha;
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb)
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     float x[16];
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
-      x[idx] = exp2f(fmaf(s[idx], cs, -m_use));
+      x[idx] = fast_exp2(fmaf(s[idx], cs, -m_use));  // v_exp_f32: results below 2^-126 flush to 0
       lsum += x[idx];
     }
     // P^T operand of k-step ss: k-slot 8 hh + i <-> key 16 ss + 4 hh + i (i < 4) and
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   if (!qvalid) return;
   const int64_t t = (int64_t)q0 + qi;
   const float f = lrow > 0.f ? 1.f / lrow : 0.f;
-  if (a.lse && hh == 0) a.lse[t * a.N + h] = lrow > 0.f ? (m + log2f(lrow)) * kLn2 : -INFINITY;
+  if (a.lse && hh == 0) a.lse[t * a.N + h] = lrow > 0.f ? (m + fast_log2(lrow)) * kLn2 : -INFINITY;
   uint16_t* orow = a.o + t * a.o_s_tok + (int64_t)h * a.o_s_head;
 #pragma unroll
   for (int vb = 0; vb < 4; ++vb)
