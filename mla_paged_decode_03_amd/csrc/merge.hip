@@ -99,12 +99,15 @@ __device__ __forceinline__ void load8(const void* p, bool fp32, float* x) {
   }
 }
 
+// One row per lpr lanes (lpr a power of two covering D / 8 chunks of 8 values, at most 64),
+// so a wave merges 64 / lpr rows at once when D is small.
 __global__ __launch_bounds__(256) void merge_two_kernel(void* out, float* out_lse, const void* po,
                                                         const float* plse, const void* so,
                                                         const float* slse, int64_t rows, int D,
-                                                        int fp32) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + w;
+                                                        int fp32, int lpr) {
+  const int rpw = 64 / lpr;  // rows per wave
+  const int w = threadIdx.x >> 6, lw = threadIdx.x & 63, l = lw & (lpr - 1);
+  const int64_t r = ((int64_t)blockIdx.x * 4 + w) * rpw + lw / lpr;
   if (r >= rows) return;
   const float lp = plse[r], ls = slse[r];
   const float m = fmaxf(lp, ls);
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(256) void merge_two_kernel(void* out, float* out_ls
     wsf /= z;
   }
   const int esz = fp32 ? 4 : 2;
-  for (int c = 8 * l; c < D; c += 512) {
+  for (int c = 8 * l; c < D; c += 8 * lpr) {
     float x[8], y[8];
     const int64_t off = (r * D + c) * esz;
     load8((const char*)po + off, fp32, x);
@@ -160,9 +163,12 @@ hipError_t launch_merge_two(void* out, float* out_lse, const void* prefix_o, con
                             const void* suffix_o, const float* suffix_lse, int64_t rows, int32_t D,
                             bool fp32, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  int lpr = 1;
+  while (lpr < 64 && 8 * lpr < D) lpr *= 2;
+  const int64_t rows_per_wg = 4 * (64 / lpr);
+  const dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)), block(256);
   hipLaunchKernelGGL(merge_two_kernel, grid, block, 0, stream, out, out_lse, prefix_o, prefix_lse,
-                     suffix_o, suffix_lse, rows, D, (int)fp32);
+                     suffix_o, suffix_lse, rows, D, (int)fp32, lpr);
   return hipGetLastError();
 }
 
