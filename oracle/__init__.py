@@ -15,6 +15,8 @@ tiling and no reordering beyond what the definitions state:
 * ``attention`` W_UK absorption, latent attention over a paged cache (with the
   causal window of multi-token verify), W_UV up-projection, the LSE merge, and
   the compute-friendly MHA path used to cross-check the absorbed one.
+* ``bmm8``      the fp8 W_UK / W_UV batched GEMMs: per-tensor weight quantisation,
+  per-token group-of-128 activation quantisation, the scaled product.
 * ``plan``      an independent re-derivation of the split-KV work plan and of
   the page -> physical row expansion, for bit-exact comparison.
 
