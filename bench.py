@@ -108,9 +108,11 @@ def algorithmic_work(w, seq_lens, with_lse):
     return out
 
 
-def cpu_baseline(inp, o_gpu, budget_s, q_scale=None):
+def cpu_baseline(inp, o_gpu, budget_s, q_scale=None, fp8_bmm=False):
     """The fp64 oracle, as it stands, on the requests of the batch in order (repeated passes)
-    until budget_s seconds of oracle time are used."""
+    until budget_s seconds of oracle time are used.  With fp8_bmm the absorption and the
+    up-projection are the oracle's fp8 BMMs (weights quantised by the oracle, before the
+    timed part)."""
     from oracle import attention as A
     from oracle.formats import bf16_to_f64
     w = inp.w
@@ -123,6 +125,11 @@ def cpu_baseline(inp, o_gpu, budget_s, q_scale=None):
         q_nope = bf16_to_f64(inp.q_nope)
         W_UK = bf16_to_f64(inp.W_UK)
         W_UV = bf16_to_f64(inp.W_UV)
+        if fp8_bmm:
+            from oracle import bmm8 as Q8
+            from oracle.formats import to_bf16_bits
+            ck, sk = Q8.quant_weight(inp.W_UK, "uk")
+            cv, sv = Q8.quant_weight(inp.W_UV, "uv")
     else:
         ql = bf16_to_f64(inp.q)
     qpe = bf16_to_f64(inp.q_pe)
@@ -142,13 +149,18 @@ def cpu_baseline(inp, o_gpu, budget_s, q_scale=None):
         for b in range(w.B):
             sl = slice(b * w.Sq, (b + 1) * w.Sq)
             t0 = time.perf_counter()
-            if w.absorb:
+            if w.absorb and fp8_bmm:
+                # the decode consumes bf16 ql_nope: the oracle's fp8 product, rounded to bf16
+                ql_b = bf16_to_f64(to_bf16_bits(Q8.absorb_fp8(inp.q_nope[sl], ck, sk)))
+            elif w.absorb:
                 ql_b = A.absorb(q_nope[sl], W_UK)
             else:
                 ql_b = ql[sl]
             o, _ = A.latent_attention(ql_b, qpe[sl], inp.cache, w.kv_dtype, inp.kv_scale,
                                       inp.block_table[b:b + 1], inp.seq_lens[b:b + 1], w.Sq, w.scale)
-            if w.absorb:
+            if w.absorb and fp8_bmm:
+                o = Q8.up_fp8(to_bf16_bits(o), cv, sv)
+            elif w.absorb:
                 o = A.up_proj(o, W_UV)
             t_used += time.perf_counter() - t0
             done.append(b)
@@ -341,6 +353,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--fp8-bmm", action="store_true",
+                    help="workloads with absorb / up-projection: run them as fp8 BMMs (per-tensor fp8 "
+                         "weights quantised once before timing, per-token group-of-128 activations)")
     ap.add_argument("--q8", action="store_true",
                     help="fp8 cache only: quantise the query to fp8 (static per-tensor scale) and "
                          "run the fp8-query decode")
@@ -363,6 +378,9 @@ def main():
     from mla_paged_decode_03_amd import inputs as gen
 
     w = gen.workload(args.workload)
+    if args.fp8_bmm and not w.absorb:
+        print("--fp8-bmm needs a workload with absorb / up-projection (verify)", file=sys.stderr)
+        sys.exit(2)
     if args.q8 and w.kv_dtype != "fp8":
         print("--q8 needs a workload with an fp8 cache", file=sys.stderr)
         sys.exit(2)
@@ -393,6 +411,13 @@ def main():
         W_UV = bf16(inp.W_UV)
         ql = torch.empty((T, N, LKV), dtype=torch.bfloat16, device=dev)
         o_up = torch.empty((T, N, w.V), dtype=torch.bfloat16, device=dev)
+        if args.fp8_bmm:  # weight quantisation happens once, at load time: outside the timing
+            W_K8 = torch.empty((N, LKV, w.P), dtype=torch.uint8, device=dev)
+            W_V8 = torch.empty((N, w.V, LKV), dtype=torch.uint8, device=dev)
+            wsk = torch.empty(1, dtype=torch.float32, device=dev)
+            wsv = torch.empty(1, dtype=torch.float32, device=dev)
+            api.mla_quant_weight_fp8(W_UK, "uk", W_K8, wsk)
+            api.mla_quant_weight_fp8(W_UV, "uv", W_V8, wsv)
     else:
         ql = bf16(inp.q)
     q_scale, q8 = None, None
@@ -416,9 +441,21 @@ def main():
         else:
             api.mla_decode_attend(plan, ql, q_pe, cache, bt, sl, w.scale, inp.kv_scale, o_lat, lse, ws)
 
+    def absorb():
+        if args.fp8_bmm:
+            api.mla_absorb_q_fp8(q_nope, W_K8, wsk, ql)
+        else:
+            api.mla_absorb_q(q_nope, W_UK, ql)
+
+    def up():
+        if args.fp8_bmm:
+            api.mla_up_v_fp8(o_lat, W_V8, wsv, o_up)
+        else:
+            api.mla_up_v(o_lat, W_UV, o_up)
+
     def step(ev=None):
         if w.absorb:
-            api.mla_absorb_q(q_nope, W_UK, ql)
+            absorb()
         if args.q8:
             api.mla_concat_quant_q(ql, q_pe, q_scale, q8)
         if ev is not None:
@@ -430,7 +467,7 @@ def main():
         if ev is not None:
             ev[2].record()
         if w.absorb:
-            api.mla_up_v(o_lat, W_UV, o_up)
+            up()
 
     for _ in range(args.warmup):
         step()
@@ -475,6 +512,10 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K * 1e3
     dec_us = timed(attend)
+    absorb_us = up_us = None
+    if w.absorb:
+        absorb_us = timed(absorb, cover=True)
+        up_us = timed(up, cover=True)
     red_us = timed(lambda: api.mla_decode_reduce(plan, o_lat, lse, ws), cover=True)
     step_dec_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
 
@@ -539,6 +580,9 @@ def main():
         "decode_kernel_us": round(dec_us, 2), "reduce_kernel_us": round(red_us, 2),
         "decode_in_step_us": round(step_dec_us, 2),
         "cache_write_us": round(wr_us, 2),
+        "absorb_us": None if absorb_us is None else round(absorb_us, 2),
+        "up_proj_us": None if up_us is None else round(up_us, 2),
+        "fp8_bmm": bool(args.fp8_bmm),
         "decode_kernel_cold_us": None if cold_us is None else round(cold_us, 2),
         "hbm_gbps": round(hbm_gbs, 1), "tflops": round(tflops, 1),
         "frac_hbm": round(hbm_gbs / HBM_PEAK_GBS, 4), "frac_mfma": round(tflops / mfma_peak, 4),
@@ -553,7 +597,7 @@ def main():
         torch.cuda.synchronize()
         o_dev = o_up if w.absorb else o_lat
         o_np = o_dev.float().cpu().numpy().astype(np.float64)
-        base, parity = cpu_baseline(inp, o_np, args.cpu_budget, q_scale)
+        base, parity = cpu_baseline(inp, o_np, args.cpu_budget, q_scale, args.fp8_bmm)
         line["cpu_baseline"] = base
         line["parity_sample"] = parity
     plan.destroy()

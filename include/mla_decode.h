@@ -364,6 +364,45 @@ int mla_chunked_prefill(const void* q_nope, const void* q_pe, const void* kv_c, 
                         int32_t V, float scale, int64_t workspace_tokens, void* o, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ---- fp8 W_UK / W_UV BMMs ----
+ *
+ * vLLM mla/common.py and mla_attention, process_weights_after_loading with the ROCm
+ * fp8 BMM: the weights are laid out per head, W_K = W_UK as [N, Lkv, P] and
+ * W_V = W_UV as [N, V, Lkv], quantised to e4m3fn with one scale for the whole tensor;
+ * the absorption and the up-projection quantise their activations per token in
+ * groups of 128 along the contracted dimension and run an fp8 batched GEMM.
+ */
+
+/*
+ * mla_quant_weight_fp8 -- one weight tensor to fp8, once, at load time.
+ *  W      bf16 [Lkv, N, X], contiguous: W_UK (X = P, which = 0) or W_UV (X = V, which = 1).
+ *  W8     e4m3fn bytes, written as W_K [N, Lkv, P] (which = 0) or W_V [N, V, Lkv] (which = 1).
+ *  w_scale  device fp32[1] receiving the dequantisation scale.
+ * Arithmetic (the page's, on bf16 tensors: fp32 compute, bf16 rounding to nearest even):
+ * amax = max |W| (at least 1e-10), s = bf16(448 / amax), y = bf16(W * s) clamped to
+ * +-448, W8 = e4m3fn(y) to nearest even; w_scale = fp32(1 / s).  Runs as one workgroup
+ * (no atomics, no scratch memory); one-time work, not on the per-step path.
+ */
+int mla_quant_weight_fp8(const void* W, int32_t Lkv, int32_t N, int32_t X, int32_t which, void* W8,
+                         float* w_scale, void* stream);
+
+/*
+ * mla_absorb_q_fp8 -- ql_nope[t,h,l] = w_scale * sum_g d[t,h,g] sum_{p in g} q8[t,h,p] W_K[h,l,p]
+ * mla_up_v_fp8     -- o[t,h,v]       = w_scale * sum_g d[t,h,g] sum_{l in g} x8[t,h,l] W_V[h,v,l]
+ *  Activations (q_nope [T,N,P] / o_latent [T,N,Lkv], contiguous bf16) are quantised in
+ *  groups g of 128 contracted elements per (token, head) (the page's "a per token group
+ *  prequant", group_size 128; its arithmetic is not printed, reading taken: the weights'
+ *  formula in fp32): amax = max |a| (at least 1e-10), s = 448 / amax, codes =
+ *  e4m3fn(clamp(a * s, +-448)) to nearest even, d = 1 / s.  Weights and w_scale as
+ *  written by mla_quant_weight_fp8.  Outputs contiguous bf16, fp32 accumulation.
+ *  P (absorb) and Lkv (up) must be multiples of 128.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.  No allocation, no host synchronisation.
+ */
+int mla_absorb_q_fp8(const void* q_nope, const void* W_K, const float* w_scale, void* ql_nope, int32_t T,
+                     int32_t N, int32_t P, int32_t Lkv, void* stream);
+int mla_up_v_fp8(const void* o_latent, const void* W_V, const float* w_scale, void* o, int32_t T, int32_t N,
+                 int32_t Lkv, int32_t V, void* stream);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* mla_last_error(void);
 

@@ -62,6 +62,9 @@ _SIGS = {
     "mla_gather_context": [_vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64,
                            _vp, _i64, _vp],
     "mla_kv_b_proj": [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
+    "mla_quant_weight_fp8": [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp],
+    "mla_absorb_q_fp8": [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp],
+    "mla_up_v_fp8": [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp],
     "mla_chunked_prefill_workspace_size": [_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i64, C.POINTER(_sz)],
     "mla_chunked_prefill": [_vp, _vp, _vp, _vp, _pi32, _pi32, _i32, _vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp,
                             _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i64, _vp, _vp, _vp, _sz, _vp],
@@ -435,6 +438,42 @@ def mla_chunked_prefill(q_nope, q_pe, kv_c, k_pe, new_lens, ctx_lens, cache, blo
         cache.shape[1], dt, float(kv_scale), block_table.data_ptr(), block_table.stride(0), W_UK.data_ptr(),
         W_UV.data_ptr(), N, W_UK.shape[0], P, q_pe.shape[2], V, float(scale), int(workspace_tokens),
         o.data_ptr(), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mla_quant_weight_fp8(W, which: str, W8, w_scale, stream=None):
+    """W_UK [Lkv,N,P] (which "uk") -> W_K [N,Lkv,P], or W_UV [Lkv,N,V] ("uv") -> W_V [N,V,Lkv],
+    e4m3fn (float8_e4m3fn or uint8 tensor W8); w_scale: device float32 [1]."""
+    _need_contig_bf16(W)
+    _need(W8, (torch.float8_e4m3fn, torch.uint8), "W8")
+    _need(w_scale, (torch.float32,), "w_scale")
+    Lkv, N, X = W.shape
+    want = (N, Lkv, X) if which == "uk" else (N, X, Lkv)
+    if tuple(W8.shape) != want or not W8.is_contiguous():
+        raise ValueError(f"W8 must be contiguous {want}")
+    _check(_lib.mla_quant_weight_fp8(W.data_ptr(), Lkv, N, X, 0 if which == "uk" else 1, W8.data_ptr(),
+                                     w_scale.data_ptr(), _stream(stream)))
+
+
+def mla_absorb_q_fp8(q_nope, W_K, w_scale, ql_nope, stream=None):
+    """ql_nope [T,N,Lkv] = fp8 BMM of q_nope [T,N,P] with W_K [N,Lkv,P] (e4m3fn) and w_scale."""
+    _need_contig_bf16(q_nope, ql_nope)
+    _need(W_K, (torch.float8_e4m3fn, torch.uint8), "W_K")
+    _need(w_scale, (torch.float32,), "w_scale")
+    T, N, P = q_nope.shape
+    Lkv = W_K.shape[1]
+    _check(_lib.mla_absorb_q_fp8(q_nope.data_ptr(), W_K.data_ptr(), w_scale.data_ptr(), ql_nope.data_ptr(),
+                                 T, N, P, Lkv, _stream(stream)))
+
+
+def mla_up_v_fp8(o_latent, W_V, w_scale, o, stream=None):
+    """o [T,N,V] = fp8 BMM of o_latent [T,N,Lkv] with W_V [N,V,Lkv] (e4m3fn) and w_scale."""
+    _need_contig_bf16(o_latent, o)
+    _need(W_V, (torch.float8_e4m3fn, torch.uint8), "W_V")
+    _need(w_scale, (torch.float32,), "w_scale")
+    T, N, Lkv = o_latent.shape
+    V = W_V.shape[1]
+    _check(_lib.mla_up_v_fp8(o_latent.data_ptr(), W_V.data_ptr(), w_scale.data_ptr(), o.data_ptr(),
+                             T, N, Lkv, V, _stream(stream)))
 
 
 def exported_symbols():

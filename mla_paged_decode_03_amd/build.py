@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmla_decode.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["plan.cpp", "abi.hip", "decode.hip", "merge.hip", "gemm.hip", "quant.hip", "cache_write.hip", "prefill.hip"]
+SOURCES = ["plan.cpp", "abi.hip", "decode.hip", "merge.hip", "gemm.hip", "quant.hip", "cache_write.hip", "prefill.hip", "bmm8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANGXX = "/opt/rocm/lib/llvm/bin/clang++"
 ARCH = "gfx950"

@@ -857,4 +857,71 @@ int mla_chunked_prefill(const void* q_nope, const void* q_pe, const void* kv_c, 
   return merge_attn_states(o, lse, o_ctx, l_ctx, o_new, l_new, (int32_t)T, N, V, MLA_DT_BF16, stream);
 }
 
+// ---------------------------------------------------------------------------------
+// fp8 W_UK / W_UV BMMs
+// ---------------------------------------------------------------------------------
+
+int mla_quant_weight_fp8(const void* W, int32_t Lkv, int32_t N, int32_t X, int32_t which, void* W8,
+                         float* w_scale, void* stream) {
+  if (!W || !W8 || !w_scale) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (Lkv < 1 || N < 1 || X < 8 || X % 8) return fail(MLA_ERR_INVALID_ARG, "bad sizes (X a multiple of 8)");
+  if (which != 0 && which != 1) return fail(MLA_ERR_INVALID_ARG, "which must be 0 (W_UK) or 1 (W_UV)");
+  if (!aligned(W, 16) || !aligned(W8, 8)) return fail(MLA_ERR_INVALID_ARG, "W must be 16-byte and W8 8-byte aligned");
+  hipError_t e = mla::launch_quant_weight((const uint16_t*)W, Lkv, N, X, which, (uint8_t*)W8, w_scale,
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "weight quantisation launch");
+}
+
+int mla_absorb_q_fp8(const void* q_nope, const void* W_K, const float* w_scale, void* ql_nope, int32_t T,
+                     int32_t N, int32_t P, int32_t Lkv, void* stream) {
+  if (!q_nope || !W_K || !w_scale || !ql_nope) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (T < 0 || N < 1 || P < 128 || Lkv < 8) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (P % 128 || Lkv % 8) return fail(MLA_ERR_UNSUPPORTED, "P must be a multiple of 128 and Lkv of 8");
+  if (!aligned(q_nope, 16) || !aligned(W_K, 16) || !aligned(ql_nope, 16))
+    return fail(MLA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  mla::Bmm8Args g{};
+  g.A = (const uint16_t*)q_nope;  // (h, t, p) at t*N*P + h*P + p
+  g.a_sh = P;
+  g.a_sm = (int64_t)N * P;
+  g.B = (const uint8_t*)W_K;  // (h, l, p) at h*Lkv*P + l*P + p
+  g.b_sh = (int64_t)Lkv * P;
+  g.b_sn = P;
+  g.C = (uint16_t*)ql_nope;  // (h, t, l) at t*N*Lkv + h*Lkv + l
+  g.c_sh = Lkv;
+  g.c_sm = (int64_t)N * Lkv;
+  g.w_scale = w_scale;
+  g.H = N;
+  g.M = T;
+  g.Nn = Lkv;
+  g.K = P;
+  hipError_t e = mla::launch_bmm8(g, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "fp8 absorb launch");
+}
+
+int mla_up_v_fp8(const void* o_latent, const void* W_V, const float* w_scale, void* o, int32_t T, int32_t N,
+                 int32_t Lkv, int32_t V, void* stream) {
+  if (!o_latent || !W_V || !w_scale || !o) return fail(MLA_ERR_INVALID_ARG, "null pointer");
+  if (T < 0 || N < 1 || V < 8 || Lkv < 128) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
+  if (Lkv % 128 || V % 8) return fail(MLA_ERR_UNSUPPORTED, "Lkv must be a multiple of 128 and V of 8");
+  if (!aligned(o_latent, 16) || !aligned(W_V, 16) || !aligned(o, 16))
+    return fail(MLA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  mla::Bmm8Args g{};
+  g.A = (const uint16_t*)o_latent;  // (h, t, l) at t*N*Lkv + h*Lkv + l
+  g.a_sh = Lkv;
+  g.a_sm = (int64_t)N * Lkv;
+  g.B = (const uint8_t*)W_V;  // (h, v, l) at h*V*Lkv + v*Lkv + l
+  g.b_sh = (int64_t)V * Lkv;
+  g.b_sn = Lkv;
+  g.C = (uint16_t*)o;  // (h, t, v) at t*N*V + h*V + v
+  g.c_sh = V;
+  g.c_sm = (int64_t)N * V;
+  g.w_scale = w_scale;
+  g.H = N;
+  g.M = T;
+  g.Nn = V;
+  g.K = Lkv;
+  hipError_t e = mla::launch_bmm8(g, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "fp8 up-projection launch");
+}
+
 }  // extern "C"

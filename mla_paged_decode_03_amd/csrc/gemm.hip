@@ -9,7 +9,8 @@
 // One workgroup (4 waves) computes a 128 or 64 (m) x 128 (n) tile of one head and
 // walks K in chunks of 128 staged through LDS.  The MFMA computes the tile
 // transposed (rows = n, columns = m) so that each lane ends up with 4
-// consecutive n of one m, which it stores as 8 bytes.  B is either
+// consecutive n of one m; the output tile goes back through LDS so that rows
+// leave as 256-byte pieces (N, P, V and Lkv are multiples of 8).  B is either
 // k-contiguous (W_UK: [Lkv][N][P], k = p) or n-contiguous (W_UV: [Lkv][N][V],
 // k = l); the latter is transposed 8x8 in registers on its way into LDS.
 #include "common.h"
@@ -114,20 +115,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
     __syncthreads();
   }
-  uint16_t* C = g.C + (int64_t)h * g.c_sh;
+  // Epilogue through LDS (the B tile's space, free after the last barrier): each lane's
+  // 4 consecutive n of one m go to the tile as 8 bytes; then rows leave as 16-byte pieces,
+  // 16 lanes per 256-byte row piece, instead of 8-byte pieces spread over 32 rows.
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + 32 * mb + l32;
-    if (m >= g.M) continue;
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const int n = n0 + 32 * w + 8 * gq + 4 * hh;
-      if (n >= g.Nn) continue;
-      u32x2_t pk;
-      pk[0] = pack_bf16x2(acc[mb][4 * gq], acc[mb][4 * gq + 1]);
-      pk[1] = pack_bf16x2(acc[mb][4 * gq + 2], acc[mb][4 * gq + 3]);
-      *(u32x2_t*)(C + (int64_t)m * g.c_sm + n) = pk;
+      const int ml = 32 * mb + l32, nl = 32 * w + 8 * gq + 4 * hh;
+      *(u32x2_t*)(sb + tile_off(ml, nl >> 3) + 2 * (nl & 4)) =
+          u32x2_t{pack_bf16x2(acc[mb][4 * gq], acc[mb][4 * gq + 1]), pack_bf16x2(acc[mb][4 * gq + 2], acc[mb][4 * gq + 3])};
     }
+  __syncthreads();
+  uint16_t* C = g.C + (int64_t)h * g.c_sh;
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int u = tid + 256 * i, ml = u >> 4, c = u & 15;
+    const int m = m0 + ml, n = n0 + 8 * c;
+    if (m < g.M && n < g.Nn) *(u32x4_t*)(C + (int64_t)m * g.c_sm + n) = *(const u32x4_t*)(sb + tile_off(ml, c));
   }
 }
 

@@ -138,4 +138,21 @@ struct GatherArgs {
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, int32_t B, int32_t max_q, hipStream_t stream);
 hipError_t launch_gather_ctx(const GatherArgs& a, bool fp8, hipStream_t stream);
 
+// fp8 batched GEMM: C[h][m][n] = w_scale * sum_g d[h][m][g] sum_{k in g} A8[h][m][k] W8[h][n][k],
+// A bf16 (h,m,k) at h*a_sh + m*a_sm + k, quantised per (m, group of 128 k) in the kernel;
+// B e4m3fn (h,n,k) at h*b_sh + n*b_sn + k (bytes); C bf16 (h,m,n) at h*c_sh + m*c_sm + n.
+struct Bmm8Args {
+  const uint16_t* A;
+  int64_t a_sh, a_sm;
+  const uint8_t* B;
+  int64_t b_sh, b_sn;
+  uint16_t* C;
+  int64_t c_sh, c_sm;
+  const float* w_scale;  // device, one value
+  int32_t H, M, Nn, K;
+};
+hipError_t launch_bmm8(const Bmm8Args& g, hipStream_t stream);
+hipError_t launch_quant_weight(const uint16_t* W, int32_t Lkv, int32_t N, int32_t X, int32_t which,
+                               uint8_t* out, float* w_scale, hipStream_t stream);
+
 }  // namespace mla

@@ -53,3 +53,9 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     m, e = np.frexp(x)
     return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
 
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Bit patterns of round_to_bf16(x) (the upper half of the float32 holding it)."""
+    v = round_to_bf16(x).astype(np.float32)
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
