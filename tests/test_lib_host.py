@@ -169,3 +169,95 @@ def test_concat_and_cache_argument_errors():
     assert call(cp=576) == api.MLA_ERR_INVALID_ARG            # page stride below a page
     assert call(kv=p16 + 2) == api.MLA_ERR_INVALID_ARG        # misaligned
     assert call(ps=0) == api.MLA_ERR_INVALID_ARG
+
+
+def _buf16(n=8192):
+    buf = (C.c_uint8 * n)()
+    return buf, (C.cast(buf, C.c_void_p).value + 255) // 256 * 256
+
+
+def test_prefill_attention_argument_errors():
+    keep, p = _buf16()
+    f = api._lib.mla_prefill_attention
+    ok = dict(qn=p, qns=128, qnh=128, qp=p, qps=64, qph=64, kn=p, kns=128, knh=128, kp=p, kps=64, v=p, vs=128,
+              vh=128, cq=p, ck=p, B=1, mq=1, N=1, P=128, R=64, V=128, causal=1, scale=0.1, o=p, os=128, oh=128)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["qn"], a["qns"], a["qnh"], a["qp"], a["qps"], a["qph"], a["kn"], a["kns"], a["knh"], a["kp"],
+                 a["kps"], a["v"], a["vs"], a["vh"], a["cq"], a["ck"], a["B"], a["mq"], a["N"], a["P"], a["R"],
+                 a["V"], a["causal"], a["scale"], a["o"], a["os"], a["oh"], None, None)
+    assert call(cq=None) == api.MLA_ERR_INVALID_ARG
+    assert call(P=64) == api.MLA_ERR_UNSUPPORTED and call(V=64) == api.MLA_ERR_UNSUPPORTED
+    for s in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(scale=s) == api.MLA_ERR_INVALID_ARG
+    assert call(vh=120) == api.MLA_ERR_INVALID_ARG       # head stride below V
+    assert call(kps=60) == api.MLA_ERR_INVALID_ARG       # rope row shorter than R
+    assert call(os=132, oh=132) == api.MLA_ERR_INVALID_ARG  # not 16-byte rows
+    assert call(o=p + 2) == api.MLA_ERR_INVALID_ARG
+    assert call(N=0) == api.MLA_ERR_INVALID_ARG
+
+
+def test_gather_and_kv_b_proj_argument_errors():
+    keep, p = _buf16()
+    g = api._lib.mla_gather_context
+    ok = dict(c=p, pe=p, sp=576 * 16, st=576, ps=16, dt=api.MLA_DT_BF16, s=1.0, bt=p, bts=4, starts=p, cu=p, B=1,
+              tot=1, okv=p, okvs=512, ope=p, opes=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["c"], a["pe"], a["sp"], a["st"], a["ps"], a["dt"], a["s"], a["bt"], a["bts"], a["starts"],
+                 a["cu"], a["B"], a["tot"], a["okv"], a["okvs"], a["ope"], a["opes"], None)
+    assert call(cu=None) == api.MLA_ERR_INVALID_ARG
+    assert call(dt=api.MLA_DT_FP32) == api.MLA_ERR_UNSUPPORTED
+    assert call(dt=api.MLA_DT_FP8_E4M3FN, s=0.0) == api.MLA_ERR_INVALID_ARG
+    assert call(st=500) == api.MLA_ERR_INVALID_ARG and call(okvs=500) == api.MLA_ERR_INVALID_ARG
+    assert call(okv=p + 2) == api.MLA_ERR_INVALID_ARG
+    k = api._lib.mla_kv_b_proj
+    assert k(p, 512, p, p, p, p, 4, 2, 512, 12, 128, None) == api.MLA_ERR_UNSUPPORTED
+    assert k(p, 100, p, p, p, p, 4, 2, 512, 128, 128, None) == api.MLA_ERR_INVALID_ARG
+    assert k(None, 512, p, p, p, p, 4, 2, 512, 128, 128, None) == api.MLA_ERR_INVALID_ARG
+
+
+def test_chunked_prefill_workspace_size_and_errors():
+    # the chunk schedule: with k requests that have context, mcc = workspace_tokens / k
+    # rounded down to the page size; mcc = 0 is a workspace error
+    with pytest.raises(api.MLAError) as e:
+        api.mla_chunked_prefill_workspace_size([1, 1, 1], [5, 5, 5], 8, 128, 128, 16, 2)
+    assert e.value.status == api.MLA_ERR_WORKSPACE
+    no_ctx = api.mla_chunked_prefill_workspace_size([7, 9], [0, 0], 8, 128, 128, 16, 64)
+    ctx = api.mla_chunked_prefill_workspace_size([7, 9], [100, 0], 8, 128, 128, 16, 64)
+    more = api.mla_chunked_prefill_workspace_size([70, 90], [100, 0], 8, 128, 128, 16, 64)
+    assert 0 < no_ctx < ctx < more
+    # the k_nope / v buffers cover the larger of the new tokens and the largest chunk
+    small = api.mla_chunked_prefill_workspace_size([1], [64], 8, 128, 128, 16, 64)
+    big = api.mla_chunked_prefill_workspace_size([1], [64], 8, 128, 128, 16, 128)
+    assert big == small  # one chunk of 64 either way
+    keep, p = _buf16()
+    f = api._lib.mla_chunked_prefill
+    nl = np.array([2], np.int32)
+    cl = np.array([0], np.int32)
+    pi = nl.ctypes.data_as(C.POINTER(C.c_int32))
+    pc = cl.ctypes.data_as(C.POINTER(C.c_int32))
+    args = [p, p, p, p, pi, pc, 1, p, p, 576 * 16, 576, 16, 0, 1.0, p, 4, p, p, 2, 512, 128, 64, 128, 0.1, 64, p,
+            None, p, 1 << 20, None]
+    a = list(args)
+    a[0] = None
+    assert f(*a) == api.MLA_ERR_INVALID_ARG
+    a = list(args)
+    a[20] = 64  # P
+    assert f(*a) == api.MLA_ERR_UNSUPPORTED
+
+
+def test_fp8_bmm_argument_errors():
+    keep, p = _buf16()
+    q = api._lib.mla_quant_weight_fp8
+    assert q(p, 512, 2, 128, 2, p, p, None) == api.MLA_ERR_INVALID_ARG   # which
+    assert q(p, 512, 2, 12, 0, p, p, None) == api.MLA_ERR_INVALID_ARG    # X not a multiple of 8
+    assert q(p + 2, 512, 2, 128, 0, p, p, None) == api.MLA_ERR_INVALID_ARG
+    a = api._lib.mla_absorb_q_fp8
+    assert a(p, p, None, p, 1, 2, 128, 512, None) == api.MLA_ERR_INVALID_ARG  # w_scale
+    assert a(p, p, p, p, 1, 2, 192, 512, None) == api.MLA_ERR_UNSUPPORTED    # P not a multiple of 128
+    u = api._lib.mla_up_v_fp8
+    assert u(p, p, p, p, 1, 2, 500, 128, None) == api.MLA_ERR_UNSUPPORTED    # Lkv not a multiple of 128
+    assert u(p, p, p, p, 1, 2, 512, 12, None) == api.MLA_ERR_UNSUPPORTED     # V not a multiple of 8
