@@ -9,19 +9,18 @@
 // a mask, and the chunk outputs are merged by LSE; the new tokens attend to themselves
 // causally, and one last merge combines the two.
 //
-// Attention kernel.  One workgroup (4 waves, one per SIMD) per (request, block of 256
-// queries, head); wave w owns queries 64w..64w+63 as two blocks of 32, one query per lane
-// column in each.  Per tile of 32 keys and per query block:
+// Attention kernel.  One workgroup (4 waves, two workgroups per CU) per (request, head,
+// block of 128 queries), dealt to the XCDs so that the query blocks of one head share an
+// L2; wave w owns queries 32w..32w+31, one per lane column.  Per tile of 32 keys:
 //   S^T[key][query] = K[key][:] . Q[query][:]     (12 MFMAs 32x32x16, K from LDS)
 //   online softmax per query (the 16 logits of a lane plus its partner lane l^32)
-//   O^T[v][query]  += V^T[v][key] . P^T[key][query] (8 MFMAs, V^T from LDS)
+//   O^T[v][query]  += V^T[v][key] . P^T[key][query] (8 MFMAs)
 // so every per-query quantity (maximum, row sum, rescale factor) is a per-lane scalar.
-// Each K and V^T fragment read from LDS feeds the MFMAs of both query blocks: at one
-// block per wave the LDS reads alone (1 KB per MFMA per wave) would match the MFMA rate.
-// K sits in LDS as [key][192] rows of 400 bytes and V transposed as [v][32 keys] rows of
-// 72 bytes: both strides make the 16-lane (b128) and 32-lane (b64) reads of one MFMA
-// operand hit distinct banks.  The next tile is loaded into registers while the current
-// one is computed.
+// K sits in LDS as [key][192] rows of 400 bytes (the 16 lanes of a b128 read hit distinct
+// banks) and V row-major as [key][128] rows of 272 bytes, read as V^T by transposing LDS
+// reads (the 4 rows of one read land 64 bytes apart in the banks); the QK takes the K rows
+// in a permuted key order so that P^T needs no shuffle.  The next tile is loaded into
+// registers while the current one is computed.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,16 +30,36 @@ namespace {
 
 constexpr int kPT = 32;          // keys per tile
 constexpr int kKRow = 200;       // bf16 per K row in LDS (192 + 8 pad): 400 bytes
-constexpr int kVRow = 36;        // bf16 per V^T row in LDS (32 keys + 4 pad): 72 bytes
+constexpr int kVRow = 136;       // bf16 per V row in LDS (128 values + 8 pad): 272 bytes
 constexpr int kPN = 128;         // P (k_nope / q_nope width)
 constexpr int kPR = 64;          // R (rope width)
 constexpr int kPV = 128;         // V (value width)
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// S^T row i of the QK MFMA holds tile key pi(i): then the 8 keys of P.V k-step s in lane
+// half h are {16s + h + 4e} and {16s + 2 + h + 4e} (e = 0..3), the 4-key strides that
+// one transposing LDS read delivers.
+__device__ __forceinline__ int pi_key(int i) { return ((i >> 2) & 3) + 4 * (i & 3) + 16 * (i >> 4); }
+
+// 8 bf16 of V^T (this lane's value column, 8 keys) from the row-major V tile: two
+// ds_read_b64_tr_b16 (16-lane group: lane j addresses row x + 4(j / 4), columns
+// 4(j % 4) .. +3 and receives column j of rows x, x+4, x+8, x+12).
+__device__ __forceinline__ u32x4_t read_vt(const uint16_t* p0, const uint16_t* p1) {
+  const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)(const void*)p0);
+  const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const lds_char*)(const void*)p1);
+  const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
+  return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+}
 
 constexpr float kRescaleAt = 8.f;  // log2 units a tile maximum may exceed the reference by
 
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[kPT * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[kPV * kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[kPT * kVRow];
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by launch index, so
   // launch index L takes work item (L % 8) * per + L / 8.  Each XCD then runs a contiguous
   // range of (request, head, query block) items: the query blocks of one head share that
@@ -84,11 +103,11 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   const int kkey = tid >> 3, kc0 = 3 * (tid & 7);
   const uint16_t* pn = a.k_nope + ((int64_t)k0 + kkey) * a.kn_s_tok + (int64_t)h * a.kn_s_head;
   const uint16_t* pp = a.k_pe + ((int64_t)k0 + kkey) * a.kp_s_tok;
-  const int vq = (tid >> 4) & 7, vo = tid & 15;
-  const uint16_t* pv = a.v + ((int64_t)k0 + 4 * vq) * a.v_s_tok + (int64_t)h * a.v_s_head + 8 * vo;
+  const int vkey = tid >> 4, vc = tid & 15;  // V: keys vkey and vkey + 16, chunk vc of 16
+  const uint16_t* pv = a.v + ((int64_t)k0 + vkey) * a.v_s_tok + (int64_t)h * a.v_s_head + 8 * vc;
   const int64_t step_n = (int64_t)kPT * a.kn_s_tok, step_p = (int64_t)kPT * a.kp_s_tok;
   const int64_t step_v = (int64_t)kPT * a.v_s_tok;
-  u32x4_t rk[3], rv[4];
+  u32x4_t rk[3], rv[2];
   auto load = [&](int kt) __attribute__((always_inline)) {
     const bool full = kt * kPT + kPT <= Sk;  // (uniform) every key of the tile exists
 #pragma unroll
@@ -97,12 +116,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       rk[i] = u32x4_t{0, 0, 0, 0};
       if (full || kt * kPT + kkey < Sk) rk[i] = c < 16 ? *(const u32x4_t*)(pn + 8 * c) : *(const u32x4_t*)(pp + 8 * (c - 16));
     }
-    if (tid < 128) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rv[r] = u32x4_t{0, 0, 0, 0};
-        if (full || kt * kPT + 4 * vq + r < Sk) rv[r] = *(const u32x4_t*)(pv + r * a.v_s_tok);
-      }
+    for (int r = 0; r < 2; ++r) {
+      rv[r] = u32x4_t{0, 0, 0, 0};
+      if (full || kt * kPT + vkey + 16 * r < Sk) rv[r] = *(const u32x4_t*)(pv + 16 * r * a.v_s_tok);
     }
     pn += step_n;
     pp += step_p;
@@ -111,17 +128,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) *(u32x4_t*)(sk + kkey * kKRow + 8 * (kc0 + i)) = rk[i];
-    if (tid < 128) {
-      // value c of keys 4vq .. 4vq+3 -> V^T row 8vo + c: the 16-bit halves of two dwords
-      // joined by one byte permute each
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t w01 = __builtin_amdgcn_perm(rv[1][c >> 1], rv[0][c >> 1], sel);
-        const uint32_t w23 = __builtin_amdgcn_perm(rv[3][c >> 1], rv[2][c >> 1], sel);
-        *(u32x2_t*)(sv + (8 * vo + c) * kVRow + 4 * vq) = u32x2_t{w01, w23};
-      }
-    }
+    for (int r = 0; r < 2; ++r) *(u32x4_t*)(sv + (vkey + 16 * r) * kVRow + 8 * vc) = rv[r];
   };
 
   f32x16_t o[4];
@@ -134,30 +142,34 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   // is rescaled rarely; lsum is this half's row sum.
   float m = -INFINITY, lsum = 0.f;
   const float cs = a.scale_log2;
+  const int krow = pi_key(l32);  // K row this lane feeds to the QK MFMA
+  // transposing-read address of this lane (elements): row hh + 4((l % 16) / 4), columns
+  // 16 ((l / 16) % 2) + 4 (l % 4) of a 32-value block; k-step ss adds 16 rows, the second
+  // read of a k-step 2 rows, value block vb 32 columns
+  const int vtr = (hh + 4 * ((l & 15) >> 2)) * kVRow + 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
   auto tile = [&](int kt) __attribute__((always_inline)) {
     // all K fragments of the tile are read before the MFMA chain starts, so that no MFMA
     // waits for an LDS round trip
     u32x4_t kf[12];
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) kf[ks] = *(const u32x4_t*)(sk + l32 * kKRow + 16 * ks + 8 * hh);
+    for (int ks = 0; ks < 12; ++ks) kf[ks] = *(const u32x4_t*)(sk + krow * kKRow + 16 * ks + 8 * hh);
     f32x16_t s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) s = mfma32(kf[ks], qf[ks], s);
-    u32x4_t vf[8];  // V^T fragments, read while the softmax runs
+    u32x4_t vf[8];  // V^T fragments (value block i / 2, k-step i % 2), read while the softmax runs
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint16_t* vr = sv + (32 * (i >> 1) + l32) * kVRow + 16 * (i & 1) + 4 * hh;
-      const u32x2_t lo = *(const u32x2_t*)vr, hi = *(const u32x2_t*)(vr + 8);
-      vf[i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      const uint16_t* p0 = sv + vtr + 16 * (i & 1) * kVRow + 32 * (i >> 1);
+      vf[i] = read_vt(p0, p0 + 2 * kVRow);
     }
-    // lane holds keys 8 gq + 4 hh + e of the tile (index 4 gq + e) for query qi
+    // lane holds S^T rows 8 gq + 4 hh + e (index 4 gq + e), tile keys pi of those, for query qi
     if (kt * kPT + kPT > unmasked) {  // (uniform) a tile on the diagonal or past Sk
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        const int j = kt * kPT + 8 * (idx >> 2) + 4 * hh + (idx & 3);
+        const int j = kt * kPT + pi_key(8 * (idx >> 2) + 4 * hh + (idx & 3));
         if (j > qlim || j >= Sk) s[idx] = -INFINITY;
       }
     }
@@ -182,8 +194,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       x[idx] = fast_exp2(fmaf(s[idx], cs, -m_use));  // v_exp_f32: results below 2^-126 flush to 0
       lsum += x[idx];
     }
-    // P^T operand of k-step ss: k-slot 8 hh + i <-> key 16 ss + 4 hh + i (i < 4) and
-    // 16 ss + 8 + 4 hh + (i - 4) (i >= 4): accumulator indices 8 ss .. 8 ss + 7
+    // P^T operand of k-step ss: accumulator indices 8 ss .. 8 ss + 7, which hold keys
+    // 16 ss + hh + 4e and 16 ss + 2 + hh + 4e, the keys of the two transposing reads
     u32x4_t pb[2];
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss)
