@@ -655,8 +655,10 @@ int mla_gather_context(const void* cache_kv_c, const void* cache_k_pe, int64_t c
 // rocBLAS handle of the current device, made on first use (kv_b_proj is a plain GEMM of
 // S latent rows by all heads' weights, which a library GEMM tiles far larger than the
 // per-head kernel of gemm.hip).
+static std::mutex g_blas_mu;  // guards the handle table and each stream-set + GEMM enqueue
+
 static rocblas_handle blas_handle(int* rc) {
-  static std::mutex mu;
+  std::mutex& mu = g_blas_mu;
   static std::vector<rocblas_handle> handles;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -664,7 +666,7 @@ static rocblas_handle blas_handle(int* rc) {
     *rc = hip_fail(e, "hipGetDevice");
     return nullptr;
   }
-  std::lock_guard<std::mutex> lk(mu);
+  std::lock_guard<std::mutex> lk(mu);  // released on return; the caller takes it again to enqueue
   if ((int)handles.size() <= dev) handles.resize(dev + 1, nullptr);
   if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success) {
     handles[dev] = nullptr;
@@ -687,6 +689,9 @@ int mla_kv_b_proj(const void* kv_c, int64_t kv_c_s_tok, const void* W_UK, const 
   int rc = MLA_OK;
   rocblas_handle hb = blas_handle(&rc);
   if (!hb) return rc;
+  // one handle per device: its stream and the two GEMMs are set and enqueued under the
+  // lock, so calls from several threads on different streams do not interleave
+  std::lock_guard<std::mutex> lk(g_blas_mu);
   if (rocblas_set_stream(hb, (hipStream_t)stream) != rocblas_status_success)
     return fail(MLA_ERR_INTERNAL, "rocblas_set_stream failed");
   // Row-major C[s][h*W + w] = sum_l kv_c[s][l] * Wt[l][h*W + w] is, in rocBLAS's column-major
