@@ -271,3 +271,25 @@ def test_workspace_too_small_is_rejected(torch_cuda):
     with pytest.raises(api.MLAError) as e:
         api.mla_decode_run(plan, q, qpe, cache, bt, sl, 0.1, 1.0, o, None, ws)
     assert e.value.status == api.MLA_ERR_WORKSPACE
+
+
+def test_causal_flatten_on_gpu(torch_cuda):
+    """Multi-token verify: query row t of an Sq = 4 decode equals an Sq = 1 decode of the
+    same query over seq_len - 3 + t keys (the causal window of the rocm_aiter_mla page's
+    multi-token decode).  Both unsplit (num_cus = 1), so the keys go through the same tiles
+    in the same order: at most one bf16 rounding apart, LSE to fp32 rounding."""
+    import copy
+    import dataclasses
+    lens = np.array([300, 97, 64], np.int32)
+    inp = gen_case("tiny", seq_lens=lens, B=3, Sq=4, N=16, page_size=16, pool_pages=None, seed=29)
+    o4, l4, _ = run_decode(torch_cuda, inp, num_cus=1)
+    for t in range(4):
+        one = copy.deepcopy(inp)
+        one.w = dataclasses.replace(inp.w, Sq=1)
+        one.seq_lens = (lens - 3 + t).astype(np.int32)
+        one.q = np.ascontiguousarray(inp.q.reshape(3, 4, 16, 512)[:, t])
+        one.q_pe = np.ascontiguousarray(inp.q_pe.reshape(3, 4, 16, 64)[:, t])
+        o1, l1, _ = run_decode(torch_cuda, one, num_cus=1)
+        a = o4.reshape(3, 4, 16, 512)[:, t]
+        assert np.all(np.abs(a - o1) <= 2.0 ** -8 * np.maximum(np.abs(a), np.abs(o1)) + 1e-6), t
+        assert np.max(np.abs(l4.reshape(3, 4, 16)[:, t] - l1)) <= 1e-5, t
