@@ -288,7 +288,8 @@ int mla_concat_and_cache(const void* kv_c, int64_t kv_c_s_tok, const void* k_pe,
  * keys), otherwise all Sk_b keys.
  *  q_nope [T,N,P], q_pe [T,N,R], k_nope [S,N,P], k_pe [S,R] (one rope row per key,
  *  shared by the heads), v [S,N,V]: bf16, strides in elements (token, head), rows
- *  16-byte aligned.  max_q >= max_b Sq_b.  scale (finite, > 0) multiplies the logits.
+ *  16-byte aligned; key and value token strides below 2^25 elements.  max_q >= max_b Sq_b.
+ *  scale (finite, > 0) multiplies the logits.
  *  o [T,N,V] bf16 receives sum softmax * v; lse [T,N] fp32 (t*N + h, natural log,
  *  scale included) or NULL.  A query with no key gets o = 0, lse = -inf.
  * Errors: INVALID_ARG (null pointers, strides, alignment), UNSUPPORTED (P, R, V),

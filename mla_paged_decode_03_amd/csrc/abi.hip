@@ -575,6 +575,9 @@ int mla_prefill_attention(const void* q_nope, int64_t q_nope_s_tok, int64_t q_no
       k_nope_s_tok < (int64_t)N * k_nope_s_head || k_pe_s_tok < R || v_s_tok < (int64_t)N * v_s_head ||
       o_s_tok < (int64_t)N * o_s_head)
     return fail(MLA_ERR_INVALID_ARG, "bad stride");
+  // the kernel addresses a tile's rows by 32-bit byte offsets from a per-tile base
+  if (k_nope_s_tok >= (1 << 25) || k_pe_s_tok >= (1 << 25) || v_s_tok >= (1 << 25))
+    return fail(MLA_ERR_UNSUPPORTED, "key / value token strides must be below 2^25 elements");
   const int64_t st[] = {q_nope_s_tok, q_nope_s_head, q_pe_s_tok, q_pe_s_head, k_nope_s_tok, k_nope_s_head,
                         k_pe_s_tok, v_s_tok, v_s_head, o_s_tok, o_s_head};
   for (int64_t x : st)

@@ -101,10 +101,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   // 24 (16 of k_nope, 8 of k_pe).  V: threads 0..127 cover 4 keys x 8 values each, which
   // are transposed on the way to LDS.  Row pointers advance by one tile per load.
   const int kkey = tid >> 3, kc0 = 3 * (tid & 7);
-  const uint16_t* pn = a.k_nope + ((int64_t)k0 + kkey) * a.kn_s_tok + (int64_t)h * a.kn_s_head;
-  const uint16_t* pp = a.k_pe + ((int64_t)k0 + kkey) * a.kp_s_tok;
   const int vkey = tid >> 4, vc = tid & 15;  // V: keys vkey and vkey + 16, chunk vc of 16
-  const uint16_t* pv = a.v + ((int64_t)k0 + vkey) * a.v_s_tok + (int64_t)h * a.v_s_head + 8 * vc;
+  // Workgroup-uniform tile bases (advanced by one tile per load) and fixed 32-bit lane
+  // offsets, so that the loads take the scalar-base form and need no 64-bit lane math.
+  const uint16_t* kn_base = a.k_nope + (int64_t)k0 * a.kn_s_tok + (int64_t)h * a.kn_s_head;
+  const uint16_t* kp_base = a.k_pe + (int64_t)k0 * a.kp_s_tok;
+  const uint16_t* v_base = a.v + (int64_t)k0 * a.v_s_tok + (int64_t)h * a.v_s_head;
+  // byte offsets (a zero-extended 32-bit lane offset on a uniform base is the scalar-base form)
+  const uint32_t kn_off = (uint32_t)(2 * kkey * a.kn_s_tok), kp_off = (uint32_t)(2 * kkey * a.kp_s_tok);
+  const uint32_t v_off0 = (uint32_t)(2 * (vkey * a.v_s_tok + 8 * vc)), v_off1 = v_off0 + (uint32_t)(32 * a.v_s_tok);
   const int64_t step_n = (int64_t)kPT * a.kn_s_tok, step_p = (int64_t)kPT * a.kp_s_tok;
   const int64_t step_v = (int64_t)kPT * a.v_s_tok;
   u32x4_t rk[3], rv[2];
@@ -114,16 +119,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     for (int i = 0; i < 3; ++i) {
       const int c = kc0 + i;
       rk[i] = u32x4_t{0, 0, 0, 0};
-      if (full || kt * kPT + kkey < Sk) rk[i] = c < 16 ? *(const u32x4_t*)(pn + 8 * c) : *(const u32x4_t*)(pp + 8 * (c - 16));
+      if (full || kt * kPT + kkey < Sk)
+        rk[i] = c < 16 ? *(const u32x4_t*)((const char*)kn_base + (kn_off + 16u * c))
+                       : *(const u32x4_t*)((const char*)kp_base + (kp_off + 16u * (c - 16)));
     }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      rv[r] = u32x4_t{0, 0, 0, 0};
-      if (full || kt * kPT + vkey + 16 * r < Sk) rv[r] = *(const u32x4_t*)(pv + 16 * r * a.v_s_tok);
-    }
-    pn += step_n;
-    pp += step_p;
-    pv += step_v;
+    if (full || kt * kPT + vkey < Sk) rv[0] = *(const u32x4_t*)((const char*)v_base + v_off0);
+    else rv[0] = u32x4_t{0, 0, 0, 0};
+    if (full || kt * kPT + vkey + 16 < Sk) rv[1] = *(const u32x4_t*)((const char*)v_base + v_off1);
+    else rv[1] = u32x4_t{0, 0, 0, 0};
+    kn_base += step_n;
+    kp_base += step_p;
+    v_base += step_v;
   };
   auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll

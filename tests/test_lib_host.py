@@ -196,6 +196,7 @@ def test_prefill_attention_argument_errors():
     assert call(os=132, oh=132) == api.MLA_ERR_INVALID_ARG  # not 16-byte rows
     assert call(o=p + 2) == api.MLA_ERR_INVALID_ARG
     assert call(N=0) == api.MLA_ERR_INVALID_ARG
+    assert call(vs=1 << 25, kns=1 << 25) == api.MLA_ERR_UNSUPPORTED  # 32-bit tile row offsets
 
 
 def test_gather_and_kv_b_proj_argument_errors():
