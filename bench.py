@@ -12,7 +12,7 @@ dominant kernel (the decode kernel, timed with HIP events on the stream it is
 launched on) and the CPU fp64 oracle timed on a bounded sample of the same batch.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3|longtail|verify|fp8|tiny]
-  python bench.py --workload prefill   # chunked prefill (compute-friendly form), DSV3 heads
+  python bench.py --workload prefill [--fp8-cache]   # chunked prefill (compute-friendly form), DSV3 heads
   python bench.py --calibrate-copy     # a plain device copy of known size, for counter scaling
 
 roofline.traffic is the decode kernel's HBM bytes per launch from rocprofv3 FETCH_SIZE and
@@ -203,6 +203,8 @@ def bench_prefill(args):
     from mla_paged_decode_03_amd import inputs as gen
     cfg = dict(gen.PREFILL_WORKLOAD)
     wt = cfg.pop("workspace_tokens")
+    if args.fp8_cache:
+        cfg["kv_dtype"] = "fp8"
     t_gen = time.perf_counter()
     inp = gen.generate_prefill(**cfg)
     t_gen = time.perf_counter() - t_gen
@@ -353,6 +355,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--fp8-cache", action="store_true",
+                    help="prefill workload: the context cache in fp8 e4m3 (dequantised by the gather)")
     ap.add_argument("--fp8-bmm", action="store_true",
                     help="workloads with absorb / up-projection: run them as fp8 BMMs (per-tensor fp8 "
                          "weights quantised once before timing, per-token group-of-128 activations)")

@@ -216,16 +216,19 @@ def test_chunked_prefill_workspace_errors(torch_cuda):
     assert e.value.status == api.MLA_ERR_WORKSPACE
 
 
-def test_prefill_workload_sampled_parity(torch_cuda):
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_prefill_workload_sampled_parity(torch_cuda, kv_dtype):
     """The full chunked-prefill workload (DSV3 heads, 4 requests of 2048 new tokens after
     6144 tokens of context, 3 context chunks each) in the launch configuration the bench
-    times; sampled (request, head) pairs against the oracle, each over all of the
-    request's new tokens (heads are independent: the oracle gets that head's slice)."""
+    times, with a bf16 and an fp8 context cache; sampled (request, head) pairs against the
+    oracle, each over all of the request's new tokens (heads are independent: the oracle
+    gets that head's slice)."""
     from mla_paged_decode_03_amd import inputs as gen
     from oracle import prefill as PF
     from oracle.formats import bf16_to_f64
     cfg = dict(gen.PREFILL_WORKLOAD)
     wt = cfg.pop("workspace_tokens")
+    cfg["kv_dtype"] = kv_dtype
     inp = gen.generate_prefill(**cfg)
     o, lse = run_prefill(torch_cuda, inp, wt)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
