@@ -47,13 +47,16 @@ KERNEL_SOURCES = ("decode.hip", "common.h", "kernels.h", "plan.h")
 COPY_BYTES = 1 << 30  # calibration copy: reads and writes this many bytes
 
 
-def kernel_digest():
-    """sha256 over the sources the decode kernel is built from."""
+def kernel_digest(sources=KERNEL_SOURCES):
+    """sha256 over the sources a kernel is built from (by default the decode kernel's)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "mla_paged_decode_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ("prefill.hip", "common.h", "kernels.h")
 
 
 def load_traffic(workload):
@@ -69,7 +72,7 @@ def load_traffic(workload):
                 k, v = ln.split(":", 1)
                 rec[k.strip()] = v.strip()
     try:
-        if rec.get("kernel_sources_sha256") != kernel_digest():
+        if rec.get("kernel_sources_sha256") != kernel_digest(PREFILL_SOURCES if workload == "prefill" else KERNEL_SOURCES):
             return None
         return float(rec["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
@@ -289,7 +292,8 @@ def bench_prefill(args):
                    "page_size": inp.ctx.w.page_size, "kv_dtype": inp.ctx.w.kv_dtype, "workspace_tokens": wt,
                    "chunk_tokens": int(mcc)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None if args.fp8_cache else load_traffic("prefill")},
         "attn_chunk_kernel_us": round(attn_us, 1), "kv_b_proj_us": round(gemm_us, 1),
         "kv_b_proj_tflops": round(gemm_tflops, 1), "step_tflops": round(step_tflops, 1),
         "frac_step_mfma": round(step_tflops / BF16_PEAK_TFLOPS, 4), "algorithmic": work,
