@@ -352,9 +352,11 @@ int mla_chunked_prefill_workspace_size(const int32_t* new_lens_host, const int32
  *  Cache, block_table, kv_dtype and kv_scale as mla_decode_run.  W_UK, W_UV
  *  [Lkv,N,P] / [Lkv,N,V] contiguous bf16.  o [T,N,V] bf16 contiguous; lse [T,N] or
  *  NULL.  workspace: device, 256-byte aligned, of the size above.
- * Launches, in order: kv_b_proj and causal attention of the new tokens, then per
- * chunk gather, kv_b_proj, attention and a merge, then the final merge; all on
- * stream.  The chunk schedule goes to the workspace by one host-to-device copy
+ * Launches, in order: kv_b_proj and causal attention of the new tokens (into o and
+ * lse, or a workspace LSE, as the running state), then per chunk gather, kv_b_proj
+ * and attention, whose epilogue merges its result into the running state by LSE
+ * (the merge is associative: the pages' order up to the bf16 rounding of the
+ * intermediate states); all on stream.  The chunk schedule goes to the workspace by one host-to-device copy
  * from pageable memory.  Errors as the calls above, WORKSPACE if too small.
  */
 int mla_chunked_prefill(const void* q_nope, const void* q_pe, const void* kv_c, const void* k_pe,

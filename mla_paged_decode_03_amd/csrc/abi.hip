@@ -556,12 +556,16 @@ int mla_debug_gather_rows(mla_plan plan, const int32_t* block_table, int64_t blo
 // Chunked prefill (compute-friendly form)
 // ---------------------------------------------------------------------------------
 
-int mla_prefill_attention(const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head, const void* q_pe,
-                          int64_t q_pe_s_tok, int64_t q_pe_s_head, const void* k_nope, int64_t k_nope_s_tok,
-                          int64_t k_nope_s_head, const void* k_pe, int64_t k_pe_s_tok, const void* v,
-                          int64_t v_s_tok, int64_t v_s_head, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
-                          int32_t max_q, int32_t N, int32_t P, int32_t R, int32_t V, int32_t causal, float scale,
-                          void* o, int64_t o_s_tok, int64_t o_s_head, float* lse, void* stream) {
+// Prefill attention; with prev_o / prev_lse the output is the LSE merge of that running
+// state (same layouts as o / lse, may alias them) with this launch's attention.
+static int prefill_attention_impl(const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
+                                  const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head, const void* k_nope,
+                                  int64_t k_nope_s_tok, int64_t k_nope_s_head, const void* k_pe,
+                                  int64_t k_pe_s_tok, const void* v, int64_t v_s_tok, int64_t v_s_head,
+                                  const int32_t* cu_q, const int32_t* cu_k, int32_t B, int32_t max_q, int32_t N,
+                                  int32_t P, int32_t R, int32_t V, int32_t causal, float scale, void* o,
+                                  int64_t o_s_tok, int64_t o_s_head, float* lse, const void* prev_o,
+                                  const float* prev_lse, void* stream) {
   if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !cu_q || !cu_k || !o)
     return fail(MLA_ERR_INVALID_ARG, "null pointer");
   if (B < 0 || max_q < 0 || N < 1) return fail(MLA_ERR_INVALID_ARG, "bad sizes");
@@ -606,11 +610,25 @@ int mla_prefill_attention(const void* q_nope, int64_t q_nope_s_tok, int64_t q_no
   a.o_s_tok = o_s_tok;
   a.o_s_head = o_s_head;
   a.lse = lse;
+  a.prev_o = (const uint16_t*)prev_o;
+  a.prev_lse = prev_lse;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.N = N;
   a.causal = causal ? 1 : 0;
   hipError_t e = mla::launch_prefill_attn(a, B, max_q, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : hip_fail(e, "prefill attention launch");
+}
+
+int mla_prefill_attention(const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head, const void* q_pe,
+                          int64_t q_pe_s_tok, int64_t q_pe_s_head, const void* k_nope, int64_t k_nope_s_tok,
+                          int64_t k_nope_s_head, const void* k_pe, int64_t k_pe_s_tok, const void* v,
+                          int64_t v_s_tok, int64_t v_s_head, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
+                          int32_t max_q, int32_t N, int32_t P, int32_t R, int32_t V, int32_t causal, float scale,
+                          void* o, int64_t o_s_tok, int64_t o_s_head, float* lse, void* stream) {
+  return prefill_attention_impl(q_nope, q_nope_s_tok, q_nope_s_head, q_pe, q_pe_s_tok, q_pe_s_head, k_nope,
+                                k_nope_s_tok, k_nope_s_head, k_pe, k_pe_s_tok, v, v_s_tok, v_s_head, cu_q, cu_k, B,
+                                max_q, N, P, R, V, causal, scale, o, o_s_tok, o_s_head, lse, nullptr, nullptr,
+                                stream);
 }
 
 int mla_gather_context(const void* cache_kv_c, const void* cache_k_pe, int64_t cache_s_page, int64_t cache_s_tok,
@@ -759,7 +777,7 @@ int chunk_schedule(const int32_t* ctx, int32_t B, int32_t page_size, int64_t wor
 }
 
 struct PrefillLayout {
-  size_t meta, lat_kv, lat_pe, kn, vv, o_new, l_new, o_ctx, l_ctx, o_chk, l_chk, total;
+  size_t meta, lat_kv, lat_pe, kn, vv, l_run, total;
 };
 
 PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t N, int32_t P, int32_t V, const ChunkSched& cs) {
@@ -778,12 +796,7 @@ PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t N, int32_t P, int32_t
   L.lat_pe = take(ctx ? (size_t)cs.max_total * mla::kRope * 2 : 0);
   L.kn = take((size_t)S * N * P * 2);
   L.vv = take((size_t)S * N * V * 2);
-  L.o_new = take(ctx ? (size_t)T * N * V * 2 : 0);
-  L.l_new = take(ctx ? (size_t)T * N * 4 : 0);
-  L.o_ctx = take(ctx ? (size_t)T * N * V * 2 : 0);
-  L.l_ctx = take(ctx ? (size_t)T * N * 4 : 0);
-  L.o_chk = take(cs.n > 1 ? (size_t)T * N * V * 2 : 0);
-  L.l_chk = take(cs.n > 1 ? (size_t)T * N * 4 : 0);
+  L.l_run = take(ctx ? (size_t)T * N * 4 : 0);  // running LSE when the caller passes none
   L.total = off;
   return L;
 }
@@ -853,21 +866,21 @@ int mla_chunked_prefill(const void* q_nope, const void* q_pe, const void* kv_c, 
   void* vv = ws + L.vv;
   const bool has_ctx = cs.n > 0;
 
-  // new tokens: up-projection of their own latent rows, causal attention among them
+  // new tokens: up-projection of their own latent rows, causal attention among them.  The
+  // caller's o (and lse, or a workspace LSE) then hold the running state, into which each
+  // context chunk's attention is merged by LSE in its epilogue; the merge is associative, so
+  // this equals merging the chunks first and the new tokens last.
   rc = mla_kv_b_proj(kv_c, Lkv, W_UK, W_UV, kn, vv, (int32_t)T, N, Lkv, P, V, stream);
   if (rc != MLA_OK) return rc;
-  void* o_new = has_ctx ? (void*)(ws + L.o_new) : o;
-  float* l_new = has_ctx ? (float*)(ws + L.l_new) : lse;
-  rc = mla_prefill_attention(q_nope, (int64_t)N * P, P, q_pe, (int64_t)N * R, R, kn, (int64_t)N * P, P, k_pe, R, vv,
-                             (int64_t)N * V, V, cu_new, cu_new, B, max_q, N, P, R, V, 1, scale, o_new,
-                             (int64_t)N * V, V, l_new, stream);
+  float* l_run = lse ? lse : (has_ctx ? (float*)(ws + L.l_run) : nullptr);
+  rc = prefill_attention_impl(q_nope, (int64_t)N * P, P, q_pe, (int64_t)N * R, R, kn, (int64_t)N * P, P, k_pe, R,
+                              vv, (int64_t)N * V, V, cu_new, cu_new, B, max_q, N, P, R, V, 1, scale, o,
+                              (int64_t)N * V, V, l_run, nullptr, nullptr, stream);
   if (rc != MLA_OK || !has_ctx) return rc;
 
   // context chunks: gather (and dequantise), up-project, attend without a mask, merge
   void* lat_kv = ws + L.lat_kv;
   void* lat_pe = ws + L.lat_pe;
-  void* o_ctx = ws + L.o_ctx;
-  float* l_ctx = (float*)(ws + L.l_ctx);
   for (int i = 0; i < cs.n; ++i) {
     const int32_t* d_starts = d_meta + (B + 1) + (size_t)i * (2 * B + 1);
     const int32_t* d_cu = d_starts + B;
@@ -878,19 +891,12 @@ int mla_chunked_prefill(const void* q_nope, const void* q_pe, const void* kv_c, 
     if (rc != MLA_OK) return rc;
     rc = mla_kv_b_proj(lat_kv, mla::kLkv, W_UK, W_UV, kn, vv, (int32_t)tot, N, Lkv, P, V, stream);
     if (rc != MLA_OK) return rc;
-    void* oc = i == 0 ? o_ctx : (void*)(ws + L.o_chk);
-    float* lc = i == 0 ? l_ctx : (float*)(ws + L.l_chk);
-    rc = mla_prefill_attention(q_nope, (int64_t)N * P, P, q_pe, (int64_t)N * R, R, kn, (int64_t)N * P, P, lat_pe,
-                               mla::kRope, vv, (int64_t)N * V, V, cu_new, d_cu, B, max_q, N, P, R, V, 0, scale, oc,
-                               (int64_t)N * V, V, lc, stream);
+    rc = prefill_attention_impl(q_nope, (int64_t)N * P, P, q_pe, (int64_t)N * R, R, kn, (int64_t)N * P, P, lat_pe,
+                                mla::kRope, vv, (int64_t)N * V, V, cu_new, d_cu, B, max_q, N, P, R, V, 0, scale, o,
+                                (int64_t)N * V, V, l_run, o, l_run, stream);
     if (rc != MLA_OK) return rc;
-    if (i > 0) {
-      rc = merge_attn_states(o_ctx, l_ctx, o_ctx, l_ctx, oc, lc, (int32_t)T, N, V, MLA_DT_BF16, stream);
-      if (rc != MLA_OK) return rc;
-    }
   }
-  // the context output is the prefix, the new tokens' own output the suffix
-  return merge_attn_states(o, lse, o_ctx, l_ctx, o_new, l_new, (int32_t)T, N, V, MLA_DT_BF16, stream);
+  return MLA_OK;
 }
 
 // ---------------------------------------------------------------------------------

@@ -113,6 +113,10 @@ struct PrefillAttnArgs {
   uint16_t* o;
   int64_t o_s_tok, o_s_head;
   float* lse;
+  // optional running state (same layouts as o / lse, may alias them): the output becomes
+  // the LSE merge of that state with this launch's attention
+  const uint16_t* prev_o;
+  const float* prev_lse;
   float scale_log2;  // scale * log2(e)
   int32_t N, causal;
   int32_t q_blocks, items, per_xcd;  // set by the launcher

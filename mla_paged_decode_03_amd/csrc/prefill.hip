@@ -221,20 +221,46 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     tile(kt);
   }
 
-  // epilogue: o = O / l (bf16), lse = ln sum exp (scale included); no key -> 0, -inf
+  // epilogue: o = O / l (bf16), lse = ln sum exp (scale included); no key -> 0, -inf.
+  // With a running state (prev_o, prev_lse) the output is its LSE merge with this result:
+  // m = max(lse_p, lse), o = (e^(lse_p - m) o_p + e^(lse - m) o) / z, lse = m + ln z.
   const float lrow = half_sum(lsum);
   if (!qvalid) return;
   const int64_t t = (int64_t)q0 + qi;
-  const float f = lrow > 0.f ? 1.f / lrow : 0.f;
-  if (a.lse && hh == 0) a.lse[t * a.N + h] = lrow > 0.f ? (m + fast_log2(lrow)) * kLn2 : -INFINITY;
+  const float lse_new = lrow > 0.f ? (m + fast_log2(lrow)) * kLn2 : -INFINITY;
+  float f_new = lrow > 0.f ? 1.f / lrow : 0.f, f_prev = 0.f, lse_out = lse_new;
   uint16_t* orow = a.o + t * a.o_s_tok + (int64_t)h * a.o_s_head;
+  const uint16_t* prow = a.prev_o ? a.prev_o + t * a.o_s_tok + (int64_t)h * a.o_s_head : nullptr;
+  if (prow) {
+    const float lp = a.prev_lse[t * a.N + h];
+    const float mm = fmaxf(lp, lse_new);
+    if (mm == -INFINITY) {
+      f_new = 0.f;
+    } else {
+      const float wp = fast_exp2((lp - mm) * kLog2e), wn = fast_exp2((lse_new - mm) * kLog2e);
+      const float z = wp + wn;
+      f_prev = wp / z;
+      f_new *= wn / z;
+      lse_out = mm + fast_log2(z) * kLn2;
+    }
+  }
+  if (a.lse && hh == 0) a.lse[t * a.N + h] = lse_out;
 #pragma unroll
   for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const int v = 32 * vb + 8 * gq + 4 * hh;
-      *(u32x2_t*)(orow + v) = u32x2_t{pack_bf16x2(o[vb][4 * gq] * f, o[vb][4 * gq + 1] * f),
-                                      pack_bf16x2(o[vb][4 * gq + 2] * f, o[vb][4 * gq + 3] * f)};
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = o[vb][4 * gq + e] * f_new;
+      if (prow) {  // read before this lane's own write of the same 8 bytes (o may alias prev_o)
+        const u32x2_t pv2 = *(const u32x2_t*)(prow + v);
+        y[0] += f_prev * bf16_to_f32((uint16_t)(pv2[0] & 0xFFFF));
+        y[1] += f_prev * bf16_to_f32((uint16_t)(pv2[0] >> 16));
+        y[2] += f_prev * bf16_to_f32((uint16_t)(pv2[1] & 0xFFFF));
+        y[3] += f_prev * bf16_to_f32((uint16_t)(pv2[1] >> 16));
+      }
+      *(u32x2_t*)(orow + v) = u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     }
 }
 
