@@ -80,9 +80,10 @@ typedef struct mla_plan_s* mla_plan;
  *  stream             hipStream_t on which the plan's device upload is enqueued.
  *  plan_out           receives the plan (owned by the library until mla_plan_destroy).
  *  workspace_bytes_out  receives the workspace size mla_decode_run needs (0 if no
- *                     request is split): fp32 partial outputs and LSE.
- * Errors: INVALID_ARG (null pointers, B < 1, negative seq_len, seq_len beyond
- * max_pages_per_req*page_size, page_size < 1), UNSUPPORTED (Lkv != 512,
+ *                     request is split): the partial outputs of split requests (fp16,
+ *                     scaled per 32-row block), their LSEs and row sums (fp32).
+ * Errors: INVALID_ARG (null pointers, B < 1, negative seq_len, seq_len above 2^30
+ * or beyond max_pages_per_req*page_size, page_size < 1), UNSUPPORTED (Lkv != 512,
  * R != 64, N outside [1,128], Sq outside [1,8], other kv_dtype), HIP.
  */
 int mla_decode_plan(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t N, int32_t Lkv,

@@ -31,6 +31,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+
 }  // namespace
 
 struct mla_plan_s {
@@ -106,6 +107,7 @@ int mla_decode_plan(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t
   if (rc) return rc;
   for (int32_t b = 0; b < B; ++b) {
     if (seq_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "negative seq_len");
+    if (seq_lens_host[b] > mla::kMaxSeqLen) return fail(MLA_ERR_INVALID_ARG, "seq_len above 2^30");
     if ((int64_t)seq_lens_host[b] > (int64_t)max_pages_per_req * page_size)
       return fail(MLA_ERR_INVALID_ARG, "seq_len exceeds max_pages_per_req * page_size");
   }
@@ -130,7 +132,7 @@ int mla_decode_plan(const int32_t* seq_lens_host, int32_t B, int32_t Sq, int32_t
   p->seq_lens.assign(seq_lens_host, seq_lens_host + B);
   p->stream = (hipStream_t)stream;
   p->device = device;
-  p->ws_bytes = (size_t)p->host.num_partials * ((size_t)mla::partial_rows(Sq, N) * mla::kLkv * 4 + (size_t)Sq * N * 8);
+  p->ws_bytes = (size_t)mla::workspace_bytes(p->host.num_partials, Sq, N);
 
   const size_t nseg = p->host.segs.size();
   p->off_part = 4 * nseg;
@@ -287,9 +289,8 @@ static int attend(mla_plan plan, const Queries& q, const void* cache_kv_c, const
   a.o_s_head = o_s_head;
   a.lse = lse;
   const size_t R = (size_t)hp.Sq * hp.N;
-  a.ws_o = (float*)workspace;
-  a.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * mla::partial_rows(hp.Sq, hp.N) *
-                                                         mla::kLkv * 4)
+  a.ws_o = workspace;
+  a.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * mla::partial_o_bytes(hp.Sq, hp.N))
                        : nullptr;
   a.ws_l = workspace ? a.ws_lse + (size_t)hp.num_partials * R : nullptr;
   a.qk_scale_log2 = scale * kv_scale * (qf8 ? q.q_scale : 1.f) * 1.4426950408889634f;
@@ -365,9 +366,8 @@ int mla_decode_reduce(mla_plan plan, void* o_latent, int64_t o_s_tok, int64_t o_
   mla::MergeArgs m{};
   m.reduce = plan->d_buf + plan->off_reduce;
   m.n_reduce = (int32_t)hp.reduce.size() / 3;
-  m.ws_o = (float*)workspace;
-  m.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * mla::partial_rows(hp.Sq, hp.N) *
-                                                         mla::kLkv * 4)
+  m.ws_o = workspace;
+  m.ws_lse = workspace ? (float*)((char*)workspace + (size_t)hp.num_partials * mla::partial_o_bytes(hp.Sq, hp.N))
                        : nullptr;
   m.ws_l = workspace ? m.ws_lse + (size_t)hp.num_partials * R : nullptr;
   m.o = (uint16_t*)o_latent;

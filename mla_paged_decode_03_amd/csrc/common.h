@@ -34,6 +34,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, bf16x2_t));
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed fp16 pair (round to nearest even), one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, f16x2_t));
+}
+// Packed fp16 pair -> two floats (exact).
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2_t, w)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2_t, w)[1];
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }

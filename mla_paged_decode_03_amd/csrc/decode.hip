@@ -302,6 +302,14 @@ __device__ __forceinline__ void vadd(float& d, float a, float b) {
 __device__ __forceinline__ void vcvt_bf16x2(uint32_t& d, float lo, float hi) {
   asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
 }
+// d += lo + hi of a packed bf16 pair (a dot product with the pair (1, 1)): a row sum of
+// exactly the rounded probabilities that the P.V MFMAs multiply.  A builtin, not a
+// scheduled statement: the compiler places it and keeps the wait states it needs.
+constexpr uint32_t kBf16Ones = 0x3F803F80u;
+__device__ __forceinline__ void dot2_sum(float& d, uint32_t pk) {
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), __builtin_bit_cast(bf16x2_t, kBf16Ones), d,
+                                      false);
+}
 
 // Tile key (0..31) held by S^T accumulator row i.
 __device__ __forceinline__ int row_key(int i) { return ((i >> 2) & 3) + 4 * (i & 3) + 16 * (i >> 4); }
@@ -652,6 +660,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
     float nm = 0.f;           // exponent offset: -m_ref (0 while m_ref = -inf)
     float thr = -INFINITY;    // (m_ref + 8) / c: elements of S above it need a new reference
     float l_acc = 0.f;        // running sum over this lane's 16 keys of each tile
+    float l_rnd = 0.f;        // the same sum over the bf16-rounded probabilities
     f32x16_t O[16];           // O^T[32 cols of block cb][32 rows], in AGPRs
     acc_zero<16>(O);
     f32x16_t sc;              // S^T of the tile in QK
@@ -814,7 +823,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
           for (int v = 0; v < 16; ++v)
             if (row_key(8 * (v >> 2) + (v & 3)) >= remh) sc[v] = -INFINITY;
         }
-        float mt[5], mf, mg, mx, ar[16], ex[16], tp[8], psum = 0.f;
+        float mt[5], mf, mg, mx, ar[16], ex[16], tp[8], psum = 0.f, prnd = 0.f;
+        uint32_t pk4[4];  // P of pairs 4..7 as bf16, moved into the P.V operand after the chain
         auto slot = [&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
           // this lane's maximum: a tree of v_max3 over slots 0..3
@@ -831,8 +841,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
           if constexpr (i == 2) vmax3(mg, mt[3], mt[4], sc[15]);
           if constexpr (i == 3) vmax3(mx, mf, mg, mg);
           // pair k = elements 2k, 2k+1: fma at slot F, exp at F+1, pair sum at F+2, row sum
-          // at F+3; pairs 4..7 first (kept in fp32 until their old P.V operand is dead),
-          // then pairs 0..3, packed in place once the first k-step's MFMAs are issued
+          // and bf16 pack at F+3; pairs 4..7 first (packed into pk4 until their old P.V
+          // operand is dead), then pairs 0..3, packed in place once the first k-step's
+          // MFMAs are issued.  The exact row sum (psum) gives the LSE, the sum of the
+          // packed values (prnd) normalises the output.
           static_for<8>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             constexpr int F = k >= 4 ? 2 + 2 * (k - 4) : 14 + 2 * k;
@@ -845,11 +857,19 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
               vexp2(ex[2 * k + 1], ar[2 * k + 1]);
             }
             if constexpr (i == F + 2) vadd(tp[k], ex[2 * k], ex[2 * k + 1]);
-            if constexpr (i == F + 3) vadd(psum, psum, tp[k]);
-            if constexpr (k < 4 && i == F + 3) {
-              uint32_t pk;
-              vcvt_bf16x2(pk, ex[2 * k], ex[2 * k + 1]);
-              pq[0][k] = pk;
+            if constexpr (i == F + 3) {
+              vadd(psum, psum, tp[k]);
+              if constexpr (k < 4) {
+                uint32_t pk;
+                vcvt_bf16x2(pk, ex[2 * k], ex[2 * k + 1]);
+                pq[0][k] = pk;
+              } else {
+                vcvt_bf16x2(pk4[k - 4], ex[2 * k], ex[2 * k + 1]);
+              }
+            }
+            if constexpr (i == F + 4) {
+              dot2_sum(prnd, k < 4 ? pq[0][k] : pk4[k - 4]);
+              use(prnd);
             }
           });
         };
@@ -886,18 +906,22 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
           m_ref = m_new;
           nm = (m_ref == -INFINITY) ? 0.f : -m_ref;  // exp2(-inf) = 0 covers masked keys
           thr = (m_ref == -INFINITY) ? -INFINITY : (m_ref + kRescaleAt) / c;
-          float ps = 0.f;
+          float ps = 0.f, pr = 0.f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const float e0 = fast_exp2(fmaf(sc[2 * k], c, nm)), e1 = fast_exp2(fmaf(sc[2 * k + 1], c, nm));
+            const uint32_t pk = pack_bf16x2(e0, e1);
             ps += e0 + e1;
-            pq[k >> 2][k & 3] = pack_bf16x2(e0, e1);
+            dot2_sum(pr, pk);
+            pq[k >> 2][k & 3] = pk;
           }
           l_acc = l_acc * fac + ps;
+          l_rnd = l_rnd * fac + pr;
         } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) pq[1][k] = pack_bf16x2(ex[8 + 2 * k], ex[9 + 2 * k]);
+          for (int k = 0; k < 4; ++k) pq[1][k] = pk4[k];
           l_acc += psum;
+          l_rnd += prnd;
         }
         // rare: O holds P.V up to tile s-1, taken against the old reference
         if (__any(fac != 1.f)) {
@@ -959,13 +983,29 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
 
     // ---- epilogue: o = O * kv_scale / l, lse = ln(sum exp) ----
     if (has_rows) {
-      const float l_row = half_sum(l_acc);
+      const float l_row = half_sum(l_acc);  // exact row sum: the LSE
+      const float l_out = half_sum(l_rnd);  // sum of the rounded probabilities: normalises O
+      // split rows: the partial is stored as fp16 O * psc, psc a power of two that puts
+      // the row's largest |O| in [2^14, 2^15) (the row sum is stored with the same factor)
+      float psc = 1.f;
+      if (pidx >= 0) {
+        float am = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb) {
+          acc_fence(O[cb]);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) am = fmaxf(am, fabsf(O[cb][v]));
+        }
+        am = half_max(am);
+        const int E = am > 0.f ? __builtin_amdgcn_frexp_expf(am) : 15;
+        psc = __builtin_ldexpf(1.f, min(max(15 - E, -64), 64));
+      }
       const int ln = lane_now(), hl = ln >> 5;
       const int rl = 32 * w + (ln & 31);
       if (rl < RG) {
         const int r = row0 + rl;
         const float lse = (l_row > 0.f) ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
-        const float f = (l_row > 0.f) ? a.out_scale / l_row : 0.f;
+        const float f = (l_out > 0.f) ? a.out_scale / l_out : 0.f;
         int t, h;
         row_th(ln & 31, t, h);
         if (pidx < 0) {
@@ -986,19 +1026,23 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
         } else {
           if (hl == 0) {
             a.ws_lse[(int64_t)pidx * R + r] = lse;
-            a.ws_l[(int64_t)pidx * R + r] = l_row / a.out_scale;
+            a.ws_l[(int64_t)pidx * R + r] = l_out / a.out_scale * psc;
           }
-          // unnormalised partial block of rows row0 + 32w .. +31 (the reduce divides by the
-          // stored row sums) in accumulator order (chunk q = 4 cb + gq: 64 lanes x 4
-          // floats), so each store is 1 KB contiguous, straight from the AGPRs
-          float* pblk = a.ws_o + ((int64_t)pidx * partial_rows(a.Sq, a.N) + row0 + 32 * w) * kLkv;
+          // unnormalised, scaled partial block of rows row0 + 32w .. +31 as fp16 (the reduce
+          // divides by the stored row sums) in accumulator order: chunk pair
+          // q = 2 cb + gp holds 64 lanes x 8 values (elements 8 gp .. 8 gp + 7 of O[cb]),
+          // so each store is 1 KB contiguous
+          char* pblk = (char*)a.ws_o + ((int64_t)pidx * partial_rows(a.Sq, a.N) + row0 + 32 * w) * kLkv * 2;
 #pragma unroll
           for (int cb = 0; cb < 16; ++cb) {
             acc_fence(O[cb]);
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-              *(f32x4_t*)(pblk + 4 * (64 * (4 * cb + gq) + ln)) =
-                  f32x4_t{O[cb][4 * gq], O[cb][4 * gq + 1], O[cb][4 * gq + 2], O[cb][4 * gq + 3]};
+            for (int gp = 0; gp < 2; ++gp)
+              *(u32x4_t*)(pblk + 16 * (64 * (2 * cb + gp) + ln)) =
+                  u32x4_t{pack_f16x2(O[cb][8 * gp] * psc, O[cb][8 * gp + 1] * psc),
+                          pack_f16x2(O[cb][8 * gp + 2] * psc, O[cb][8 * gp + 3] * psc),
+                          pack_f16x2(O[cb][8 * gp + 4] * psc, O[cb][8 * gp + 5] * psc),
+                          pack_f16x2(O[cb][8 * gp + 6] * psc, O[cb][8 * gp + 7] * psc)};
           }
         }
       }

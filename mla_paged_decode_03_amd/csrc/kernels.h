@@ -23,9 +23,9 @@ struct DecodeArgs {
   uint16_t* o;                // [T, N, 512] bf16
   int64_t o_s_tok, o_s_head;
   float* lse;                 // [T, N] or null
-  float* ws_o;                // [partials, Sq*N, 512]
+  void* ws_o;                 // [partials, Sq*N rounded up to 32, 512] fp16, scaled (blocked)
   float* ws_lse;              // [partials, Sq*N]
-  float* ws_l;                // [partials, Sq*N]: row sums / kv_scale
+  float* ws_l;                // [partials, Sq*N]: row sums / kv_scale, times the block's scale
   const uint8_t* q8;          // fp8 queries [T, N, 576] e4m3fn (null: bf16 q_nope / q_pe)
   int64_t q8_s_tok, q8_s_head;  // bytes
   float qk_scale_log2;        // scale * kv_scale (* q_scale for fp8 queries) * log2(e)
@@ -36,7 +36,7 @@ struct DecodeArgs {
 struct MergeArgs {
   const int32_t* reduce;  // [n_reduce][3]: req, first partial, count
   int32_t n_reduce;
-  const float* ws_o;
+  const void* ws_o;
   const float* ws_lse;
   const float* ws_l;
   uint16_t* o;

@@ -12,15 +12,18 @@ namespace mla {
 namespace {
 
 // Split-KV reduce: one workgroup per (request, block of 32 query rows, quarter of the
-// 512 columns).  Partial i of a row holds its unnormalised output O_i = sum_j p_j v_j, its
-// row sum l_i / kv_scale and its lse_i, so o = sum_i exp(lse_i - m) O_i / l_i / z with
+// 512 columns).  Partial i of a row holds its unnormalised output O_i = sum_j p_j v_j
+// times a power-of-two block scale, as fp16, its row sum l_i / kv_scale times the same
+// scale, and its lse_i, so o = sum_i exp(lse_i - m) O_i / l_i / z with
 // z = sum_i exp(lse_i - m) (the merge above).  The partial outputs of a row block are
-// stored in the decode kernels' accumulator order: chunk q = 4 (32-column block) + gq holds 64 lanes x 4 floats, lane l
-// covering row l % 32 and columns 8 gq + 4 (l / 32) .. +3 of that column block.  Wave w
-// of column quarter z merges the 4 chunks of column block 4z + w, one 1 KB load per chunk
-// and partial (the 4 in flight together); the result goes through LDS as a bf16
-// [32][128] tile and leaves as 256-byte row pieces.
+// stored in the decode kernels' accumulator order: chunk pair q = 2 (32-column block) + gp
+// holds 64 lanes x 8 fp16 values, lane l covering row l % 32 and columns
+// 16 gp + 4 (l / 32) .. +3 and 16 gp + 8 + 4 (l / 32) .. +3 of that column block.  Wave w
+// of column quarter z merges the 2 chunk pairs of column block 4z + w: one 1 KB load per
+// pair and partial, those of up to 8 partials in flight together; the result goes
+// through LDS as a bf16 [32][128] tile and leaves as 256-byte row pieces.
 constexpr int kTileLd = 128 + 8;  // bf16 row stride of the output tile in LDS
+constexpr int kMergeBatch = 8;    // partials whose loads are in flight together
 __global__ __launch_bounds__(256) void split_merge_kernel(MergeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[32 * kTileLd];
   const int R = a.Sq * a.N;
@@ -44,29 +47,40 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeArgs a) {
     const int t = r / a.N, h = r - t * a.N;
     a.lse[((int64_t)b * a.Sq + t) * a.N + h] = dead ? -INFINITY : m + fast_log2(z) * kLn2;
   }
-  const int64_t pstride = partial_rows(a.Sq, a.N) * kLkv;
+  const int64_t pstride = partial_o_bytes(a.Sq, a.N);
   const int cb = 4 * zq + w;  // column block of this wave
-  const float* src = a.ws_o + (int64_t)base * pstride + (int64_t)(32 * rb) * kLkv + 256 * (4 * cb) + 4 * l;
-  f32x4_t acc[4] = {};
-  for (int i = 0; i < n && !dead; ++i) {
-    // the partials are unnormalised: weight exp(lse_i - m) / z over the stored row sum
-    // (row sum / kv_scale, so the value scale comes in too); rows of a partial that saw
-    // no key have lse -inf, weight 0
-    const float li = l_i[(int64_t)i * R];
-    const float wi = li > 0.f ? fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e) * inv / li : 0.f;
-    f32x4_t x[4];
+  const char* src = (const char*)a.ws_o + (int64_t)base * pstride + (int64_t)(32 * rb) * kLkv * 2 +
+                    16 * (64 * (2 * cb) + l);
+  float acc[16] = {};  // accumulator element v: column 8 (v / 4) + 4 h2 + v % 4 of the column block
+  for (int i0 = 0; i0 < n && !dead; i0 += kMergeBatch) {
+    u32x4_t x[kMergeBatch][2];
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) x[gq] = *(const f32x4_t*)(src + (int64_t)i * pstride + 256 * gq);
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (i0 + k < n) {
+        x[k][0] = *(const u32x4_t*)(src + (int64_t)(i0 + k) * pstride);
+        x[k][1] = *(const u32x4_t*)(src + (int64_t)(i0 + k) * pstride + 1024);
+      }
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq)
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (i0 + k < n) {
+        // weight exp(lse_i - m) / z over the stored row sum (which carries the value scale
+        // and the block scale); rows of a partial that saw no key have lse -inf, weight 0
+        const float li = l_i[(int64_t)(i0 + k) * R];
+        const float wi = li > 0.f ? fast_exp2((lse_i[(int64_t)(i0 + k) * R] - m) * kLog2e) * inv / li : 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[gq][e] += wi * x[gq][e];
+        for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            acc[8 * gp + 2 * d] += wi * f16_lo(x[k][gp][d]);
+            acc[8 * gp + 2 * d + 1] += wi * f16_hi(x[k][gp][d]);
+          }
+      }
   }
 #pragma unroll
   for (int gq = 0; gq < 4; ++gq) {
     const int col = 32 * w + 8 * gq + 4 * h2;  // within this quarter
-    *(u32x2_t*)(tile + rl * kTileLd + col) =
-        u32x2_t{pack_bf16x2(acc[gq][0], acc[gq][1]), pack_bf16x2(acc[gq][2], acc[gq][3])};
+    *(u32x2_t*)(tile + rl * kTileLd + col) = u32x2_t{pack_bf16x2(acc[4 * gq], acc[4 * gq + 1]),
+                                                     pack_bf16x2(acc[4 * gq + 2], acc[4 * gq + 3])};
   }
   __syncthreads();
 #pragma unroll

@@ -5,7 +5,7 @@
 // off the forward path; its rule is not shown.  This rule is the library's:
 // the keys of all requests, counted in 64-key granules, are dealt in request
 // order to at most num_cus / head_groups parts of near-equal cost, each
-// segment costing one extra granule for its query load and epilogue.  A
+// segment costing kSegCost extra granules for its query load and epilogue.  A
 // request cut between parts is computed as partial (o, lse) states that the
 // merge kernel combines.
 #include "plan.h"
@@ -61,7 +61,11 @@ bool build_plan(const int32_t* seq_lens, int32_t B, int32_t Sq, int32_t N, int32
       *err = "build_plan: negative seq_len";
       return false;
     }
-    gran[b] = (seq_lens[b] + kGranule - 1) / kGranule;
+    if (seq_lens[b] > kMaxSeqLen) {
+      *err = "build_plan: seq_len above the supported maximum (2^30 keys)";
+      return false;
+    }
+    gran[b] = (int32_t)(((int64_t)seq_lens[b] + kGranule - 1) / kGranule);
     total += gran[b] + kSegCost;
   }
   const int32_t hg = head_groups(Sq, N);
@@ -94,7 +98,7 @@ bool build_plan(const int32_t* seq_lens, int32_t B, int32_t Sq, int32_t N, int32
       Segment s;
       s.req = pc.req;
       s.kv_start = pc.g0 * kGranule;
-      s.kv_end = std::min(pc.g1 * kGranule, seq_lens[pc.req]);
+      s.kv_end = (int32_t)std::min<int64_t>((int64_t)pc.g1 * kGranule, seq_lens[pc.req]);
       s.partial = nseg[pc.req] > 1 ? base[pc.req] + seen[pc.req]++ : -1;
       out->segs.push_back(s);
     }

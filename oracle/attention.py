@@ -153,10 +153,12 @@ def mha_compute_friendly(q_nope: np.ndarray, q_pe: np.ndarray, kv_c: np.ndarray,
                          scale: float, Sq: int):
     """The compute-friendly (MHA) path for one request, for cross-checking.
 
-    ``mla/common.py`` docstring, "Compute Friendly Approach":
-    k_nope = (kv_c @ W_UK.view(Lkv, N*P)).view(Skv, N, P),
-    v = (kv_c @ W_UV.view(Lkv, N*V)).view(Skv, N, V), then per-head SDPA of
-    cat[q_nope, q_pe] against cat[k_nope, k_pe broadcast over heads], with V.
+    Follows the ``mla/common.py`` module docstring, section "Compute Friendly
+    Approach": every cache row's latent vector is up-projected per head, giving
+    the key part k_nope[j,h,:] = sum_l kv_c[j,l] W_UK[l,h,:] and the value
+    v[j,h,:] = sum_l kv_c[j,l] W_UV[l,h,:]; each head then runs plain softmax
+    attention with query [q_nope | q_pe] (width P+R) against keys [k_nope | k_pe],
+    the rope part of the key being the same for all heads.
     q_nope [Sq, N, P], q_pe [Sq, N, R], kv_c [L, Lkv], k_pe [L, R].
     Returns o [Sq, N, V], lse [Sq, N].
     """

@@ -101,10 +101,10 @@ def split_plan(seq_lens, Sq: int, N: int, num_cus: int):
 
 
 def workspace_bytes(num_partials: int, Sq: int, N: int, Lkv: int = 512) -> int:
-    """fp32 partial outputs [partials, Sq*N rounded up to whole 32-row blocks, Lkv], then
+    """fp16 partial outputs [partials, Sq*N rounded up to whole 32-row blocks, Lkv], then
     fp32 partial LSE [partials, Sq*N] and fp32 partial row sums [partials, Sq*N]."""
     rows = (Sq * N + 31) // 32 * 32
-    return num_partials * (rows * Lkv * 4 + Sq * N * 8)
+    return num_partials * (rows * Lkv * 2 + Sq * N * 8)
 
 
 def gather_rows_all(block_table, seq_lens, page_size: int):

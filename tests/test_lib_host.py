@@ -95,6 +95,7 @@ def _plan_rc(**kw):
     (dict(ps=0), api.MLA_ERR_INVALID_ARG),
     (dict(seq_lens=np.array([65], np.int32)), api.MLA_ERR_INVALID_ARG),  # > 4 pages of 16
     (dict(seq_lens=np.array([-1], np.int32)), api.MLA_ERR_INVALID_ARG),
+    (dict(seq_lens=np.array([2 ** 31 - 1], np.int32)), api.MLA_ERR_INVALID_ARG),  # above 2^30 keys
 ])
 def test_plan_argument_errors(kw, code):
     rc, msg = _plan_rc(**kw)
@@ -262,3 +263,17 @@ def test_fp8_bmm_argument_errors():
     u = api._lib.mla_up_v_fp8
     assert u(p, p, p, p, 1, 2, 500, 128, None) == api.MLA_ERR_UNSUPPORTED    # Lkv not a multiple of 128
     assert u(p, p, p, p, 1, 2, 512, 12, None) == api.MLA_ERR_UNSUPPORTED     # V not a multiple of 8
+
+
+def test_plan_compute_host_rejects_overflowing_seq_len():
+    """seq_len + 63 (the granule round-up) must not wrap: lengths above 2^30 are rejected."""
+    n_items, n_red = C.c_int32(0), C.c_int32(0)
+    for L in (2 ** 31 - 1, 2 ** 31 - 64, 2 ** 30 + 1):
+        sl = np.array([5, L], np.int32)
+        rc = api._lib.mla_plan_compute_host(sl.ctypes.data_as(C.POINTER(C.c_int32)), 2, 1, 128, 256, None,
+                                            C.byref(n_items), None, C.byref(n_red), None, None)
+        assert rc == api.MLA_ERR_INVALID_ARG and "seq_len" in api.mla_last_error()
+    sl = np.array([2 ** 30], np.int32)  # the largest accepted length plans normally
+    rc = api._lib.mla_plan_compute_host(sl.ctypes.data_as(C.POINTER(C.c_int32)), 1, 1, 128, 256, None,
+                                        C.byref(n_items), None, C.byref(n_red), None, None)
+    assert rc == api.MLA_OK and n_items.value == 256 and n_red.value == 1

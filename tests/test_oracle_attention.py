@@ -169,8 +169,9 @@ def test_merge_of_empty_states():
 
 
 def test_head_independence_with_tiled_padding():
-    """Padding heads by tiling q (rocm_aiter_mla AiterMLAHelper.get_mla_padded_q) cannot change
-    the real heads: attention is independent per query head over the shared KV."""
+    """Padding heads by tiling q (rocm_aiter_mla page, AiterMLAHelper.get_mla_padded_q) cannot
+    change the real heads: each head's output depends only on its own query row and the
+    latent cache, so extra query rows leave the others untouched."""
     B, N, Lkv, R, ps = 2, 12, 16, 8, 4
     ql, qpe, bits, bt, L = _rand_case(21, B, N, Lkv, R, ps, [13, 6])
     o, lse = A.latent_attention(ql, qpe, bits, "bf16", 1.0, bt, L, 1, 0.3, Lkv=Lkv)

@@ -86,9 +86,9 @@ def test_plan_is_independent_of_head_count_when_groups_match():
 
 
 def test_workspace_bytes():
-    assert PL.workspace_bytes(3, 1, 16) == 3 * (32 * 512 * 4 + 16 * 8)  # 16 rows -> one 32-row block
-    assert PL.workspace_bytes(2, 1, 128) == 2 * 128 * (512 * 4 + 8)
-    assert PL.workspace_bytes(1, 4, 40) == 160 * 512 * 4 + 160 * 8
+    assert PL.workspace_bytes(3, 1, 16) == 3 * (32 * 512 * 2 + 16 * 8)  # 16 rows -> one 32-row block
+    assert PL.workspace_bytes(2, 1, 128) == 2 * 128 * (512 * 2 + 8)
+    assert PL.workspace_bytes(1, 4, 40) == 160 * 512 * 2 + 160 * 8
 
 
 def test_gather_rows_all_matches_golden():
