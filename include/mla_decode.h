@@ -153,6 +153,28 @@ int mla_decode_reduce(mla_plan plan, void* o_latent, int64_t o_s_tok, int64_t o_
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_run_noalloc -- mla_decode_run for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and kernels, with the split partial states kept
+ * in a static device array of the library instead of a caller's workspace.  It calls
+ * no hipMalloc / hipFree and nothing that allocates.
+ *
+ * Arguments, ownership and errors are those of mla_decode_run without workspace /
+ * workspace_bytes.  The static array holds 64 MiB (67108864 bytes) per device, for as
+ * long as the process runs; a plan whose workspace_bytes exceeds it is rejected with
+ * MLA_ERR_WORKSPACE before anything is enqueued.  Every call on a device shares that
+ * device's array, and calls that overlap on one device (different streams, or host
+ * threads) race on it; calls on one stream are ordered and safe.  Nothing in the array
+ * needs clearing between calls: attend writes every partial state that reduce reads.
+ */
+int mla_decode_run_noalloc(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
+                           const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head, const void* cache_kv_c,
+                           const void* cache_k_pe, int64_t cache_s_page, int64_t cache_s_tok, int32_t num_pages,
+                           const int32_t* block_table, int64_t block_table_s_req, const int32_t* seq_lens,
+                           float scale, float kv_scale, void* o_latent, int64_t o_s_tok, int64_t o_s_head,
+                           float* lse, void* stream);
+
+/*
  * mla_decode_run_q8 / mla_decode_attend_q8 -- mla_decode_run / mla_decode_attend for
  * an fp8 cache with an fp8 query: q8 = [ql_nope | q_pe] quantised with the static
  * per-tensor q_scale (mla_concat_quant_q; vLLM MLAAttention quantises the decode query

@@ -40,6 +40,8 @@ _SIGS = {
     "mla_plan_destroy": [_vp],
     "mla_decode_run": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i32, _vp, _i64,
                        _vp, _f32, _f32, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
+    "mla_decode_run_noalloc": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i32, _vp, _i64,
+                               _vp, _f32, _f32, _vp, _i64, _i64, _vp, _vp],
     "mla_decode_attend": [_vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i32, _vp,
                           _i64, _vp, _f32, _f32, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
     "mla_decode_reduce": [_vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp],
@@ -190,6 +192,15 @@ def mla_decode_run(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale
     seq_lens [B] int32 (device), o_latent [T,N,512] bf16, lse [T,N] fp32 or None."""
     _check(_lib.mla_decode_run(*_decode_args(plan, q_nope, q_pe, cache, block_table, seq_lens, scale,
                                              kv_scale, o_latent, lse, workspace, stream, cache_k_pe)))
+
+
+def mla_decode_run_noalloc(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale: float,
+                           kv_scale: float, o_latent, lse=None, stream=None, cache_k_pe=None):
+    """mla_decode_run with the library's static device scratch as the workspace (no
+    allocation; plans needing more than 64 MiB of workspace are rejected)."""
+    args = _decode_args(plan, q_nope, q_pe, cache, block_table, seq_lens, scale, kv_scale, o_latent, lse,
+                        None, stream, cache_k_pe)
+    _check(_lib.mla_decode_run_noalloc(*(args[:21] + args[23:])))
 
 
 def mla_decode_attend(plan: Plan, q_nope, q_pe, cache, block_table, seq_lens, scale: float,

@@ -31,6 +31,15 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Workspace of mla_decode_run_noalloc: a static device array, one copy per device, held
+// until the process ends.  In host code `scratch` is only a stand-in symbol; its device
+// address comes from hipGetSymbolAddress, resolved once per device with that device
+// current and kept in g_scratch.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
 
 }  // namespace
 
@@ -395,6 +404,45 @@ int mla_decode_run(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int6
   if (rc) return rc;
   if (plan->host.reduce.empty()) return MLA_OK;
   return mla_decode_reduce(plan, o_latent, o_s_tok, o_s_head, lse, workspace, workspace_bytes, stream);
+}
+
+// Device address of the static scratch on the current device (resolved on first use).
+static int static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device index beyond the static scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MLA_ERR_INTERNAL, "static scratch has no device address");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MLA_OK;
+}
+
+int mla_decode_run_noalloc(mla_plan plan, const void* q_nope, int64_t q_nope_s_tok, int64_t q_nope_s_head,
+                           const void* q_pe, int64_t q_pe_s_tok, int64_t q_pe_s_head, const void* cache_kv_c,
+                           const void* cache_k_pe, int64_t cache_s_page, int64_t cache_s_tok, int32_t num_pages,
+                           const int32_t* block_table, int64_t block_table_s_req, const int32_t* seq_lens,
+                           float scale, float kv_scale, void* o_latent, int64_t o_s_tok, int64_t o_s_head,
+                           float* lse, void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARG, "null plan");
+  if (plan->ws_bytes > kStaticScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "the plan needs " + std::to_string(plan->ws_bytes) +
+                                       " bytes of workspace; the static scratch holds " +
+                                       std::to_string(kStaticScratchBytes) + " (use mla_decode_run)");
+  void* ws = nullptr;
+  if (plan->ws_bytes > 0) {
+    const int rc = static_scratch(&ws);
+    if (rc) return rc;
+  }
+  return mla_decode_run(plan, q_nope, q_nope_s_tok, q_nope_s_head, q_pe, q_pe_s_tok, q_pe_s_head, cache_kv_c,
+                        cache_k_pe, cache_s_page, cache_s_tok, num_pages, block_table, block_table_s_req, seq_lens,
+                        scale, kv_scale, o_latent, o_s_tok, o_s_head, lse, ws, plan->ws_bytes, stream);
 }
 
 int mla_decode_run_q8(mla_plan plan, const void* q8, int64_t q8_s_tok, int64_t q8_s_head, float q_scale,
