@@ -60,12 +60,10 @@ def _hip_runtime_link_args():
             lib_dir = os.path.join(os.path.dirname(spec.origin), "lib")
             hip = os.path.join(lib_dir, "libamdhip64.so")
             if os.path.exists(hip):
-                # rocBLAS (kv_b_proj) from the same directory: torch's copy, on torch's runtime
-                return [f"-L{lib_dir}", "-l:libamdhip64.so", "-l:librocblas.so", f"-Wl,-rpath,{lib_dir}",
-                        "-Wl,--disable-new-dtags"]
+                return [f"-L{lib_dir}", "-l:libamdhip64.so", f"-Wl,-rpath,{lib_dir}", "-Wl,--disable-new-dtags"]
     except Exception:
         pass
-    return ["-L/opt/rocm/lib", "-lamdhip64", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+    return ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def build(verbose: bool = False, extra=()) -> str:

@@ -8,8 +8,6 @@
 #include <string>
 #include <vector>
 
-#include <rocblas/rocblas.h>
-
 #include <mutex>
 
 #include "../../include/mla_decode.h"
@@ -721,31 +719,6 @@ int mla_gather_context(const void* cache_kv_c, const void* cache_k_pe, int64_t c
   return e == hipSuccess ? MLA_OK : hip_fail(e, "context gather launch");
 }
 
-// rocBLAS handle of the current device, made on first use (kv_b_proj is a plain GEMM of
-// S latent rows by all heads' weights, which a library GEMM tiles far larger than the
-// per-head kernel of gemm.hip).
-static std::mutex g_blas_mu;  // guards the handle table and each stream-set + GEMM enqueue
-
-static rocblas_handle blas_handle(int* rc) {
-  std::mutex& mu = g_blas_mu;
-  static std::vector<rocblas_handle> handles;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    *rc = hip_fail(e, "hipGetDevice");
-    return nullptr;
-  }
-  std::lock_guard<std::mutex> lk(mu);  // released on return; the caller takes it again to enqueue
-  if ((int)handles.size() <= dev) handles.resize(dev + 1, nullptr);
-  if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success) {
-    handles[dev] = nullptr;
-    *rc = fail(MLA_ERR_INTERNAL, "rocblas_create_handle failed");
-    return nullptr;
-  }
-  *rc = MLA_OK;
-  return handles[dev];
-}
-
 int mla_kv_b_proj(const void* kv_c, int64_t kv_c_s_tok, const void* W_UK, const void* W_UV, void* k_nope,
                   void* v, int32_t S, int32_t N, int32_t Lkv, int32_t P, int32_t V, void* stream) {
   if (!kv_c || !W_UK || !W_UV || !k_nope || !v) return fail(MLA_ERR_INVALID_ARG, "null pointer");
@@ -755,28 +728,44 @@ int mla_kv_b_proj(const void* kv_c, int64_t kv_c_s_tok, const void* W_UK, const 
   if (!aligned(kv_c, 16) || !aligned(W_UK, 16) || !aligned(W_UV, 16) || !aligned(k_nope, 16) || !aligned(v, 16))
     return fail(MLA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (S == 0) return MLA_OK;
-  int rc = MLA_OK;
-  rocblas_handle hb = blas_handle(&rc);
-  if (!hb) return rc;
-  // one handle per device: its stream and the two GEMMs are set and enqueued under the
-  // lock, so calls from several threads on different streams do not interleave
-  std::lock_guard<std::mutex> lk(g_blas_mu);
-  if (rocblas_set_stream(hb, (hipStream_t)stream) != rocblas_status_success)
-    return fail(MLA_ERR_INTERNAL, "rocblas_set_stream failed");
-  // Row-major C[s][h*W + w] = sum_l kv_c[s][l] * Wt[l][h*W + w] is, in rocBLAS's column-major
-  // terms, C^T (N*W x S) = Wt^T (N*W x Lkv) * kv_c^T (Lkv x S): no transposes, leading
-  // dimensions N*W, kv_c_s_tok and N*W.  bf16 in and out, fp32 accumulation.
-  const float one = 1.f, zero = 0.f;
+  hipError_t e;
+  if (Lkv % 32 == 0) {
+    // one launch over both weights: [S x Lkv] by [Lkv x N*P] and [Lkv x N*V]
+    mla::KvbArgs g{};
+    g.A = (const uint16_t*)kv_c;
+    g.a_s = kv_c_s_tok;
+    g.B0 = (const uint16_t*)W_UK;
+    g.B1 = (const uint16_t*)W_UV;
+    g.C0 = (uint16_t*)k_nope;
+    g.C1 = (uint16_t*)v;
+    g.N0 = N * P;
+    g.N1 = N * V;
+    g.M = S;
+    g.K = Lkv;
+    e = mla::launch_kvb_gemm(g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_b_proj launch");
+    return MLA_OK;
+  }
+  // other latent widths: the per-head GEMM, each head's weight slice against all rows
   for (int which = 0; which < 2; ++which) {
     const int32_t W = which ? V : P;
-    const int64_t NW = (int64_t)N * W;
-    const rocblas_status st = (rocblas_gemm_ex)(
-        hb, rocblas_operation_none, rocblas_operation_none, (rocblas_int)NW, S, Lkv, &one, which ? W_UV : W_UK,
-        rocblas_datatype_bf16_r, (rocblas_int)NW, kv_c, rocblas_datatype_bf16_r, (rocblas_int)kv_c_s_tok, &zero,
-        which ? v : k_nope, rocblas_datatype_bf16_r, (rocblas_int)NW, which ? v : k_nope, rocblas_datatype_bf16_r,
-        (rocblas_int)NW, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    if (st != rocblas_status_success)
-      return fail(MLA_ERR_INTERNAL, std::string("rocblas_gemm_ex failed: ") + rocblas_status_to_string(st));
+    mla::GemmArgs g{};
+    g.A = (const uint16_t*)kv_c;  // (h, m=s, k=l) at s*kv_c_s_tok + l: shared by the heads
+    g.a_sh = 0;
+    g.a_sm = kv_c_s_tok;
+    g.B = (const uint16_t*)(which ? W_UV : W_UK);  // (h, n, k=l) at l*N*W + h*W + n
+    g.b_sh = W;
+    g.b_sn = 1;
+    g.b_sk = (int64_t)N * W;
+    g.C = (uint16_t*)(which ? v : k_nope);  // (h, s, n) at s*N*W + h*W + n
+    g.c_sh = W;
+    g.c_sm = (int64_t)N * W;
+    g.H = N;
+    g.M = S;
+    g.Nn = W;
+    g.K = Lkv;
+    e = mla::launch_gemm(g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_b_proj launch");
   }
   return MLA_OK;
 }

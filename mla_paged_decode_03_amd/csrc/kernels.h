@@ -89,6 +89,20 @@ struct GemmArgs {
   int32_t H, M, Nn, K;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+// kv_b_proj: C0[s][n] = sum_k A[s][k] B0[k][n] (n < N0) and C1 likewise with B1 (n < N1),
+// bf16 with fp32 accumulation; A row stride a_s, B and C rows contiguous (stride N0 / N1).
+// K must be a multiple of 32 and N0, N1 multiples of 8 (>= 8); tile counts set by the launcher.
+struct KvbArgs {
+  const uint16_t* A;
+  int64_t a_s;
+  const uint16_t* B0;
+  const uint16_t* B1;
+  uint16_t* C0;
+  uint16_t* C1;
+  int32_t N0, N1, M, K;
+  int32_t mt, nt0, nt, per_xcd;
+};
+hipError_t launch_kvb_gemm(KvbArgs g, hipStream_t stream);
 hipError_t launch_gather_rows(const int32_t* block_table, int64_t bt_s, const int32_t* seq_lens,
                               const int64_t* offsets, int32_t B, int32_t page_size, int64_t* rows,
                               hipStream_t stream);

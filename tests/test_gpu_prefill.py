@@ -137,24 +137,54 @@ def test_gather_context(torch_cuda, kv_dtype):
             assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref))
 
 
-def test_kv_b_proj(torch_cuda):
+@pytest.mark.parametrize("S,N,P,V,Lkv,row_pad", [
+    (300, 3, 128, 128, 512, 0),   # partial tiles in s and n (N*P = 384)
+    (1, 1, 8, 16, 512, 0),        # one row, narrow weights
+    (600, 16, 128, 128, 512, 64),  # whole n tiles, strided latent rows (row stride 576)
+    (257, 2, 64, 40, 96, 0),      # three K chunks of 32, second weight narrower than a tile
+    (50, 4, 16, 24, 72, 8),       # Lkv not a multiple of 32: the per-head GEMM
+])
+def test_kv_b_proj(torch_cuda, S, N, P, V, Lkv, row_pad):
     torch = torch_cuda
     from mla_paged_decode_03_amd import api
     from oracle import prefill as PF
     from oracle.formats import bf16_to_f64
-    rng = np.random.default_rng(43)
-    S, N, P, V = 300, 3, 128, 128
-    kv = _bf16(rng, (S, 512))
-    wk, wv = _bf16(rng, (512, N, P), 0.02), _bf16(rng, (512, N, V), 0.02)
-    kn = torch.empty((S, N, P), dtype=torch.bfloat16, device="cuda")
-    vv = torch.empty((S, N, V), dtype=torch.bfloat16, device="cuda")
-    api.mla_kv_b_proj(bf16_dev(kv), bf16_dev(wk), bf16_dev(wv), kn, vv)
+    rng = np.random.default_rng(43 + S + Lkv)
+    kv = _bf16(rng, (S, Lkv + row_pad))
+    wk, wv = _bf16(rng, (Lkv, N, P), 0.02), _bf16(rng, (Lkv, N, V), 0.02)
+    kn = torch.full((S, N, P), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vv = torch.full((S, N, V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    api.mla_kv_b_proj(bf16_dev(kv)[:, :Lkv], bf16_dev(wk), bf16_dev(wv), kn, vv)
     torch.cuda.synchronize()
-    rk, rv = PF.kv_b_proj(bf16_to_f64(kv), bf16_to_f64(wk), bf16_to_f64(wv))
+    rk, rv = PF.kv_b_proj(bf16_to_f64(kv[:, :Lkv]), bf16_to_f64(wk), bf16_to_f64(wv))
     for got, ref in ((bf16_host(kn), rk), (bf16_host(vv), rv)):
         mx, rel = metrics(got, ref)
         assert mx <= O_MAX_ABS and rel <= O_REL_L2, (mx, rel)
         # fp32 accumulation, one rounding: within one bf16 step of the exact value
+        assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-6)
+
+
+def test_kv_b_proj_full_size_sampled(torch_cuda):
+    """The prefill workload's kv_b_proj shape (8192 latent rows, 128 heads, P = V = 128):
+    every output column of 256 sampled rows (spread over all s-tiles) against the oracle."""
+    torch = torch_cuda
+    from mla_paged_decode_03_amd import api
+    from oracle import prefill as PF
+    from oracle.formats import bf16_to_f64
+    rng = np.random.default_rng(4099)
+    S, N, P, V = 8192, 128, 128, 128
+    kv = _bf16(rng, (S, 512))
+    wk, wv = _bf16(rng, (512, N, P), 0.02), _bf16(rng, (512, N, V), 0.02)
+    kn = torch.full((S, N, P), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vv = torch.full((S, N, V), float("nan"), dtype=torch.bfloat16, device="cuda")
+    api.mla_kv_b_proj(bf16_dev(kv), bf16_dev(wk), bf16_dev(wv), kn, vv)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(S, 256, replace=False))
+    rk, rv = PF.kv_b_proj(bf16_to_f64(kv[rows]), bf16_to_f64(wk), bf16_to_f64(wv))
+    for got, ref in ((bf16_host(kn[torch.from_numpy(rows).cuda()]), rk),
+                     (bf16_host(vv[torch.from_numpy(rows).cuda()]), rv)):
+        mx, rel = metrics(got, ref)
+        assert mx <= O_MAX_ABS and rel <= O_REL_L2, (mx, rel)
         assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-6)
 
 
