@@ -532,14 +532,19 @@ def main():
         del graph
         return e0.elapsed_time(e1) / reps * 1e3
 
-    reps = max(K, 20)
+    # (20 repetitions: a profile of this run then averages mostly over the timed steps)
+    reps = 20
     attend_us = b2b(attend, reps)
     reduce_us = graphed(lambda: api.mla_decode_reduce(plan, o_lat, lse, ws), reps) if len(red) else 0.0
-    decode_us = attend_us + reduce_us
-    absorb_us = up_us = None
+    absorb_us = up_us = quant_us = None
     if w.absorb:
         absorb_us = graphed(absorb, reps)
         up_us = graphed(up, reps)
+    if args.q8:
+        quant_us = graphed(lambda: api.mla_concat_quant_q(ql, q_pe, q_scale, q8), reps)
+    # The decode call as it runs inside the timed steps (attend then reduce, each after the
+    # other kernels of the step): the GPU time per step less the step's other kernels.
+    decode_us = gpu_step_us - sum(x for x in (absorb_us, up_us, quant_us) if x is not None)
 
     # The cache write that precedes the decode in a serving step: this batch's T new rows
     # [kv_c | k_pe] at their slots (the last key of each request), into a scratch copy of
@@ -614,10 +619,11 @@ def main():
                    "sum_keys": int(inp.seq_lens.sum()), "absorb_up": bool(w.absorb),
                    "lse": with_lse, "q8": bool(args.q8), "q_scale": q_scale},
         "roofline": roof,
-        "roofline_scope": "mla_decode_run = attend kernel + split reduce kernel, warm, kernel durations "
-                          "from back-to-back launches (attend) and a replayed graph of launches (reduce)",
+        "roofline_scope": "mla_decode_run (attend kernel + split reduce kernel) inside the timed steps: "
+                          "GPU time per step (events around the K steps) less the step's other kernels",
         "decode_us": round(decode_us, 2), "attend_kernel_us": round(attend_us, 2),
         "reduce_kernel_us": round(reduce_us, 2), "gpu_step_us": round(gpu_step_us, 2),
+        "concat_quant_us": None if quant_us is None else round(quant_us, 2),
         "cache_write_us": round(wr_us, 2),
         "absorb_us": None if absorb_us is None else round(absorb_us, 2),
         "up_proj_us": None if up_us is None else round(up_us, 2),
