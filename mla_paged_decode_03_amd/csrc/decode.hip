@@ -615,8 +615,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
       }
     }
   } else {
+    // tiles 0 and 1 only: every workgroup starts by loading 147 KB of queries, and the
+    // start-up burst of all workgroups is what the first step waits for; the steps load
+    // one tile each from then on, two ahead of the QK, as in the steady state
 #pragma unroll 1
-    for (int k = 0; k < kStages; ++k) {
+    for (int k = 0; k < 2; ++k) {
       if (pf.si >= s_end) break;
       const DmaTile t = dma_tile<false, FAST>(a, pf, smem0 + (issued % kStages) * kStageB);
       dma_all(t);

@@ -20,8 +20,9 @@ namespace {
 // holds 64 lanes x 8 fp16 values, lane l covering row l % 32 and columns
 // 16 gp + 4 (l / 32) .. +3 and 16 gp + 8 + 4 (l / 32) .. +3 of that column block.  Wave w
 // of column quarter z merges the 2 chunk pairs of column block 4z + w: one 1 KB load per
-// pair and partial, those of up to 8 partials in flight together; the result goes
-// through LDS as a bf16 [32][128] tile and leaves as 256-byte row pieces.
+// pair and partial, all loads of up to 8 partials (with their LSEs and row sums) issued
+// together; the result goes through LDS as a bf16 [32][128] tile and leaves as 256-byte
+// row pieces.
 constexpr int kTileLd = 128 + 8;  // bf16 row stride of the output tile in LDS
 constexpr int kMergeBatch = 8;    // partials whose loads are in flight together
 __global__ __launch_bounds__(256) void split_merge_kernel(MergeArgs a) {
@@ -31,50 +32,62 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeArgs a) {
   if (red >= a.n_reduce || 32 * rb >= R) return;  // (whole workgroup)
   const int b = a.reduce[3 * red], base = a.reduce[3 * red + 1], n = a.reduce[3 * red + 2];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, rl = l & 31, h2 = l >> 5;
-  // this lane's row: reference m and 1 / sum of the weights (rows past R get none)
+  // this lane's row (rows past R read row R - 1 and are not stored)
   const int r = 32 * rb + rl;
   const float* lse_i = a.ws_lse + (int64_t)base * R + min(r, R - 1);
   const float* l_i = a.ws_l + (int64_t)base * R + min(r, R - 1);
+  const int64_t pstride = partial_o_bytes(a.Sq, a.N);
+  const int cb = 4 * zq + w;  // column block of this wave
+  const char* src = (const char*)a.ws_o + (int64_t)base * pstride + (int64_t)(32 * rb) * kLkv * 2 +
+                    16 * (64 * (2 * cb) + l);
+  // Every load of the first kMergeBatch partials is issued at once (partial outputs, LSEs
+  // and row sums), so the merge waits for one round trip, not one per dependent step.
+  u32x4_t x[kMergeBatch][2];
+  float lv[kMergeBatch], sv[kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k)
+    if (k < n) {
+      x[k][0] = *(const u32x4_t*)(src + (int64_t)k * pstride);
+      x[k][1] = *(const u32x4_t*)(src + (int64_t)k * pstride + 1024);
+      sv[k] = lse_i[(int64_t)k * R];
+      lv[k] = l_i[(int64_t)k * R];
+    }
   float m = -INFINITY;
-  if (r < R)
-    for (int i = 0; i < n; ++i) m = fmaxf(m, lse_i[(int64_t)i * R]);
-  const bool dead = (m == -INFINITY);
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k)
+    if (k < n) m = fmaxf(m, sv[k]);
+  for (int i = kMergeBatch; i < n; ++i) m = fmaxf(m, lse_i[(int64_t)i * R]);
+  const bool dead = (m == -INFINITY) || r >= R;
   float z = 0.f;
-  if (!dead)
-    for (int i = 0; i < n; ++i) z += fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e);
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k)
+    if (k < n) z += fast_exp2((sv[k] - m) * kLog2e);
+  for (int i = kMergeBatch; i < n; ++i) z += fast_exp2((lse_i[(int64_t)i * R] - m) * kLog2e);
   const float inv = dead ? 0.f : 1.f / z;
   if (a.lse && zq == 0 && w == 0 && h2 == 0 && r < R) {
     const int t = r / a.N, h = r - t * a.N;
     a.lse[((int64_t)b * a.Sq + t) * a.N + h] = dead ? -INFINITY : m + fast_log2(z) * kLn2;
   }
-  const int64_t pstride = partial_o_bytes(a.Sq, a.N);
-  const int cb = 4 * zq + w;  // column block of this wave
-  const char* src = (const char*)a.ws_o + (int64_t)base * pstride + (int64_t)(32 * rb) * kLkv * 2 +
-                    16 * (64 * (2 * cb) + l);
+  // weight exp(lse_i - m) / z over the stored row sum (which carries the value scale and
+  // the block scale); rows of a partial that saw no key have lse -inf, weight 0
   float acc[16] = {};  // accumulator element v: column 8 (v / 4) + 4 h2 + v % 4 of the column block
-  for (int i0 = 0; i0 < n && !dead; i0 += kMergeBatch) {
-    u32x4_t x[kMergeBatch][2];
+  auto add = [&](const u32x4_t (&xx)[2], float li, float lsev) __attribute__((always_inline)) {
+    const float wi = (li > 0.f && !dead) ? fast_exp2((lsev - m) * kLog2e) * inv / li : 0.f;
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k)
-      if (i0 + k < n) {
-        x[k][0] = *(const u32x4_t*)(src + (int64_t)(i0 + k) * pstride);
-        x[k][1] = *(const u32x4_t*)(src + (int64_t)(i0 + k) * pstride + 1024);
+    for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[8 * gp + 2 * d] += wi * f16_lo(xx[gp][d]);
+        acc[8 * gp + 2 * d + 1] += wi * f16_hi(xx[gp][d]);
       }
+  };
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k)
-      if (i0 + k < n) {
-        // weight exp(lse_i - m) / z over the stored row sum (which carries the value scale
-        // and the block scale); rows of a partial that saw no key have lse -inf, weight 0
-        const float li = l_i[(int64_t)(i0 + k) * R];
-        const float wi = li > 0.f ? fast_exp2((lse_i[(int64_t)(i0 + k) * R] - m) * kLog2e) * inv / li : 0.f;
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp)
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            acc[8 * gp + 2 * d] += wi * f16_lo(x[k][gp][d]);
-            acc[8 * gp + 2 * d + 1] += wi * f16_hi(x[k][gp][d]);
-          }
-      }
+  for (int k = 0; k < kMergeBatch; ++k)
+    if (k < n) add(x[k], lv[k], sv[k]);
+  for (int i = kMergeBatch; i < n; ++i) {
+    const u32x4_t xx[2] = {*(const u32x4_t*)(src + (int64_t)i * pstride),
+                           *(const u32x4_t*)(src + (int64_t)i * pstride + 1024)};
+    add(xx, l_i[(int64_t)i * R], lse_i[(int64_t)i * R]);
   }
 #pragma unroll
   for (int gq = 0; gq < 4; ++gq) {
