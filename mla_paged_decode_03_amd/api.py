@@ -437,6 +437,8 @@ def mla_chunked_prefill(q_nope, q_pe, kv_c, k_pe, new_lens, ctx_lens, cache, blo
     _need(block_table, (torch.int32,), "block_table")
     if lse is not None:
         _need(lse, (torch.float32,), "lse")
+        if not lse.is_contiguous():
+            raise ValueError("lse must be contiguous [T, N]")
     nl, cl = _host_i32(new_lens), _host_i32(ctx_lens)
     T, N, P = q_nope.shape
     V = W_UV.shape[2]

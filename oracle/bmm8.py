@@ -17,8 +17,10 @@ s = bf16(448 / amax), y = bf16(W * s), clamped to +-448, code = e4m3fn(y) rounde
 nearest even; the dequantisation scale is float32(1 / s).
 
 Activation quantisation (the pages name it, but print no arithmetic; reading taken:
-the weights' formula per group, in float32): for token m and group g of 128 consecutive
-contracted elements, amax = max |a| (at least 1e-10), s = float32(448 / amax),
+the weights' formula per group, in float32; parity unpinned: no printed value or
+reference implementation fixes it, only the quantisation invariants of the tests):
+for token m and group g of 128 consecutive contracted elements,
+amax = max |a| (at least 1e-10), s = float32(448 / amax),
 y = float32(a * s) clamped to +-448, code = e4m3fn(y); dequantisation d = float32(1 / s).
 
 Product: C[h, m, n] = w_scale * sum_g d[h, m, g] * sum_{k in g} A8[h, m, k] W8[h, n, k],

@@ -338,3 +338,41 @@ def test_canaries_around_workspace_and_output(torch_cuda):
     ro, rl = oracle(inp)
     check(bf16_host(o), lse.cpu().numpy().astype(np.float64), ro, rl)
     plan.destroy()
+
+
+@pytest.mark.parametrize("ps,L,cus", [
+    (64, 1000, 3),    # tile-aligned pages (one base per tile), segments cut at 64-key granules
+    (32, 333, 2),     # one page per tile
+    (128, 700, 5),    # two tiles per page
+    (64, 97, 0),      # one unsplit request ending inside its second tile
+    (16, 600, 3),     # pages smaller than a tile: per-row block-table lookups
+])
+def test_gather_addressing_dominant_keys(torch_cuda, ps, L, cus):
+    """The decode kernel's own addressing, without the test-only gather kernel: query head h
+    is aligned with the rope part of key j_h only, so key j_h carries all the weight (the
+    other logits trail by hundreds of log2 units and their exponentials underflow to 0)
+    and o[h] must equal that key's latent row bit for bit.  The 16 keys sit at tile,
+    page, granule and segment boundaries and in the last partial tile, so a wrong tile
+    base, lane offset or end-of-segment clamp shows as a different row.  Split plans
+    (cus > 0) also run the fp16 partials and the reduce, which keep a single key exact."""
+    from oracle.formats import bf16_to_f64
+    from mla_paged_decode_03_amd.inputs import f32_to_bf16_bits
+    inp = gen_case("tiny", seq_lens=np.array([L], np.int32), B=1, N=16, page_size=ps, pool_pages=None,
+                   seed=600 + ps + L)
+    cands = [0, 1, 31, 32, 33, 63, 64, 65, L - 1, L - 2, (L - 1) // 32 * 32, L // 2, 127, 128, 191, 192]
+    js = [min(max(j, 0), L - 1) for j in cands][:16]
+    flat = inp.cache.reshape(-1, 576)
+    rows = [int(inp.block_table[0, j // ps]) * ps + j % ps for j in js]
+    inp.q = np.zeros_like(inp.q)
+    qpe = np.zeros((1, 16, 64), np.float32)
+    for h, r in enumerate(rows):
+        kpe = bf16_to_f64(flat[r, 512:])
+        qpe[0, h] = np.sign(kpe) * (8000.0 / max(1e-6, np.abs(kpe).sum()))
+    inp.q_pe = f32_to_bf16_bits(qpe)
+    o, lse, plan = run_decode(torch_cuda, inp, num_cus=cus)
+    if cus:
+        assert plan.workspace_bytes > 0  # the request is split
+    for h, r in enumerate(rows):
+        assert np.array_equal(o[0, h], bf16_to_f64(flat[r, :512])), (h, js[h], r)
+    ro, _ = oracle(inp)
+    assert np.max(np.abs(o - ro)) <= 1e-6  # the fp64 oracle agrees (all weight on one key)
