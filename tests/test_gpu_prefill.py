@@ -47,6 +47,9 @@ def _check(o, lse, ro, rl, where=""):
 @pytest.mark.parametrize("causal,sq,sk", [
     (True, [37, 130, 1, 0, 256], [87, 330, 1, 5, 256]),
     (False, [37, 130, 1, 3, 64], [50, 0, 7, 300, 33]),
+    # unmasked launches run the pipelined kernel: odd and even tile counts (3, 5, 32)
+    # through its loop and tail steps, query blocks of 256 with ragged ends
+    (False, [300, 513, 257], [70, 160, 1000]),
 ])
 def test_prefill_attention(torch_cuda, causal, sq, sk):
     torch = torch_cuda
@@ -106,6 +109,36 @@ def test_prefill_attention_dominant_key_exact(torch_cuda):
     got = o.view(torch.int16).cpu().numpy().view(np.uint16)
     for i in np.nonzero(ok)[0]:
         assert np.array_equal(got[i], v[target[i]]), i
+
+
+def test_prefill_attention_unmasked_dominant_key_exact(torch_cuda):
+    """Unmasked launch (the pipelined kernel): each query has one key whose logit leads
+    all others by far, anywhere among 100 keys (4 tiles, the last partial) and across
+    two 256-query blocks: o equals that key's value row bitwise."""
+    torch = torch_cuda
+    from mla_paged_decode_03_amd import api
+    from mla_paged_decode_03_amd.inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(11)
+    N, P, R, V, Sq, Sk = 3, 128, 64, 128, 300, 100
+    v = _bf16(rng, (Sk, N, V))
+    kn_f = np.zeros((Sk, N, P), np.float32)
+    for j in range(Sk):
+        kn_f[j, :, j] = 1.0  # key j: a one in nope dimension j (P = 128 > Sk)
+    target = (np.arange(Sq) * 37 + 11) % Sk
+    qn_f = np.zeros((Sq, N, P), np.float32)
+    for i in range(Sq):
+        qn_f[i, :, target[i]] = 3000.0
+    qp = np.zeros((Sq, N, R), np.uint16)
+    kp = np.zeros((Sk, R), np.uint16)
+    cq = torch.tensor([0, Sq], dtype=torch.int32, device="cuda")
+    ck = torch.tensor([0, Sk], dtype=torch.int32, device="cuda")
+    o = torch.empty((Sq, N, V), dtype=torch.bfloat16, device="cuda")
+    api.mla_prefill_attention(bf16_dev(f32_to_bf16_bits(qn_f)), bf16_dev(qp), bf16_dev(f32_to_bf16_bits(kn_f)),
+                              bf16_dev(kp), bf16_dev(v), cq, ck, Sq, False, 1.0, o)
+    torch.cuda.synchronize()
+    got = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = [i for i in range(Sq) if not np.array_equal(got[i], v[target[i]])]
+    assert not bad, (len(bad), bad[:8])
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
