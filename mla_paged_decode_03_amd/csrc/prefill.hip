@@ -663,18 +663,23 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_pipe_kernel(PrefillAttnAr
   }
 
   // ---- epilogue per sub-block: o = O / l (bf16), lse = ln sum exp; with a running state
-  // (prev_o, prev_lse) its LSE merge with this result ----
+  // (prev_o, prev_lse) its LSE merge with this result.  O / l goes through LDS as fp32, 64
+  // columns at a time, so that each store writes whole 128-byte rows of o (8 lanes a row)
+  // rather than 16 bytes into each of 32 rows (partial lines, written back about three
+  // times over).  Wave w uses an 8.5 KB region of stage (ntiles + w / 2) % 4: no DMA is in
+  // flight any more, and every wave has passed the barrier after which that stage (tile
+  // ntiles - 3 or ntiles - 2, or one never filled) is read by nobody.
+  constexpr int kEpRow = 68;  // floats per staged row (64 + 4 pad: b128 accesses free of conflicts)
+  float* ep = (float*)(sm + ((ntiles + (w >> 1)) % kNStg) * kStg) + (w & 1) * (32 * kEpRow);
+  float* epf = (float*)(sm + ((ntiles + (w >> 1)) % kNStg) * kStg) + 2 * 32 * kEpRow + (w & 1) * 32;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const float lrow = half_sum(lsum[j]);
     const int qi = kQB * qb + 64 * w + 32 * j + l32;
-    if (qi >= Sq) continue;
-    const int64_t t = (int64_t)q0 + qi;
+    const int64_t t = (int64_t)q0 + min(qi, Sq - 1);
     const float lse_new = lrow > 0.f ? (m[j] + fast_log2(lrow)) * kLn2 : -INFINITY;
     float f_new = lrow > 0.f ? 1.f / lrow : 0.f, f_prev = 0.f, lse_out = lse_new;
-    uint16_t* orow = a.o + t * a.o_s_tok + (int64_t)h * a.o_s_head;
-    const uint16_t* prow = a.prev_o ? a.prev_o + t * a.o_s_tok + (int64_t)h * a.o_s_head : nullptr;
-    if (prow) {
+    if (a.prev_o && qi < Sq) {
       const float lp = a.prev_lse[t * a.N + h];
       const float mm = fmaxf(lp, lse_new);
       if (mm == -INFINITY) {
@@ -687,25 +692,49 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_pipe_kernel(PrefillAttnAr
         lse_out = mm + fast_log2(z) * kLn2;
       }
     }
-    if (a.lse && hh == 0) a.lse[t * a.N + h] = lse_out;
+    if (a.lse && hh == 0 && qi < Sq) a.lse[t * a.N + h] = lse_out;
+    if (hh == 0) epf[l32] = f_prev;
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+    for (int hf = 0; hf < 2; ++hf) {
+      // this lane's part of rows l32: columns 32 c + 8 gq + 4 hh .. +3 of the half (c = 0, 1)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int v = 32 * vb + 8 * gq + 4 * hh;
-        if (gq == 0) pv_fence(o[j][vb]);
-        float y[4];
+      for (int c = 0; c < 2; ++c) {
+        pv_fence(o[j][2 * hf + c]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = o[j][vb][4 * gq + e] * f_new;
-        if (prow) {  // read before this lane's own write of the same 8 bytes (o may alias prev_o)
-          const u32x2_t pv2 = *(const u32x2_t*)(prow + v);
-          y[0] += f_prev * bf16_to_f32((uint16_t)(pv2[0] & 0xFFFF));
-          y[1] += f_prev * bf16_to_f32((uint16_t)(pv2[0] >> 16));
-          y[2] += f_prev * bf16_to_f32((uint16_t)(pv2[1] & 0xFFFF));
-          y[3] += f_prev * bf16_to_f32((uint16_t)(pv2[1] >> 16));
-        }
-        *(u32x2_t*)(orow + v) = u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        for (int gq = 0; gq < 4; ++gq)
+          *(f32x4_t*)(ep + l32 * kEpRow + 32 * c + 8 * gq + 4 * hh) =
+              f32x4_t{o[j][2 * hf + c][4 * gq] * f_new, o[j][2 * hf + c][4 * gq + 1] * f_new,
+                      o[j][2 * hf + c][4 * gq + 2] * f_new, o[j][2 * hf + c][4 * gq + 3] * f_new};
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // s_waitcnt lgkmcnt(0): this wave's rows are in LDS
+      __builtin_amdgcn_wave_barrier();
+      // lane: row 8 k + lane / 8, columns 8 (lane % 8) .. +7 of the half
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3), cc = 8 * (lane & 7);
+        const int qr = kQB * qb + 64 * w + 32 * j + r;
+        const f32x4_t y0 = *(const f32x4_t*)(ep + r * kEpRow + cc);
+        const f32x4_t y1 = *(const f32x4_t*)(ep + r * kEpRow + cc + 4);
+        float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+        if (qr < Sq) {
+          const int64_t tr = (int64_t)q0 + qr;
+          uint16_t* dst = a.o + tr * a.o_s_tok + (int64_t)h * a.o_s_head + 64 * hf + cc;
+          if (a.prev_o) {  // read before this lane's own write of the same 16 bytes (o may alias prev_o)
+            const float fp = epf[r];
+            const u32x4_t pv4 = *(const u32x4_t*)(a.prev_o + tr * a.o_s_tok + (int64_t)h * a.o_s_head + 64 * hf + cc);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              y[2 * d] += fp * bf16_to_f32((uint16_t)(pv4[d] & 0xFFFF));
+              y[2 * d + 1] += fp * bf16_to_f32((uint16_t)(pv4[d] >> 16));
+            }
+          }
+          *(u32x4_t*)dst = u32x4_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                                   pack_bf16x2(y[6], y[7])};
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half overwrites
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
