@@ -648,19 +648,17 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_pipe_kernel(PrefillAttnAr
       pv_drain(o[1]);
     }
   };
+  // Every step is the steady-state one: the last tile's step also runs a QK, of a tile
+  // that does not exist (stale LDS into S registers nobody reads; 24 MFMAs per workgroup),
+  // so the loop is the only copy of the step and needs no separately scheduled tail.
   const std::true_type yes;
   const std::false_type no;
-  int t = 0;
-  for (; t + 2 < ntiles; t += 2) {
+  for (int t = 0; t < ntiles; t += 2) {
     step(yes, no, t, sA, sB);
-    step(yes, no, t + 1, sB, sA);
+    if (t + 1 < ntiles) step(yes, no, t + 1, sB, sA);
   }
-  if (t + 1 < ntiles) {
-    step(yes, yes, t, sA, sB);
-    step(no, yes, t + 1, sB, sA);
-  } else if (t < ntiles) {
-    step(no, yes, t, sA, sB);
-  }
+  pv_drain(o[0]);  // the wait states before anything reads or moves O
+  pv_drain(o[1]);
 
   // ---- epilogue per sub-block: o = O / l (bf16), lse = ln sum exp; with a running state
   // (prev_o, prev_lse) its LSE merge with this result.  O / l goes through LDS as fp32, 64
