@@ -9,18 +9,21 @@
 // a mask, and the chunk outputs are merged by LSE; the new tokens attend to themselves
 // causally, and one last merge combines the two.
 //
-// Attention kernel.  One workgroup (4 waves, two workgroups per CU) per (request, head,
-// block of 128 queries), dealt to the XCDs so that the query blocks of one head share an
-// L2; wave w owns queries 32w..32w+31, one per lane column.  Per tile of 32 keys:
-//   S^T[key][query] = K[key][:] . Q[query][:]     (12 MFMAs 32x32x16, K from LDS)
+// Attention, two kernels with the same per-tile arithmetic.  Per tile of 32 keys:
+//   S^T[key][query] = K[key][:] . Q[query][:]     (12 MFMAs 32x32x16 per 32 queries)
 //   online softmax per query (the 16 logits of a lane plus its partner lane l^32)
 //   O^T[v][query]  += V^T[v][key] . P^T[key][query] (8 MFMAs)
 // so every per-query quantity (maximum, row sum, rescale factor) is a per-lane scalar.
-// K sits in LDS as [key][192] rows of 400 bytes (the 16 lanes of a b128 read hit distinct
-// banks) and V row-major as [key][128] rows of 272 bytes, read as V^T by transposing LDS
-// reads (the 4 rows of one read land 64 bytes apart in the banks); the QK takes the K rows
-// in a permuted key order so that P^T needs no shuffle.  The next tile is loaded into
-// registers while the current one is computed.
+// V is read as V^T from row-major LDS rows by transposing reads, and the QK takes the K
+// rows in a permuted key order so that P^T needs no shuffle.  Query blocks of one head
+// are dealt to one XCD, so that they share its L2 for the head's K/V.
+//  - prefill_attn_kernel (causal launches): 4 waves, two workgroups per CU, blocks of
+//    128 queries, wave w owns queries 32w..32w+31; K in LDS as [key][192] rows of 400
+//    bytes, V as [key][128] rows of 272 bytes; the next tile waits in registers.
+//  - prefill_attn_pipe_kernel (unmasked launches, the context chunks): one workgroup per
+//    CU, blocks of 256 queries, each wave two sub-blocks of 32, K/V by direct-to-LDS
+//    loads into a 4-stage ring, and the QK of the next tile interleaved with the softmax
+//    (described with the kernel below).
 #include <type_traits>
 #include <utility>
 
@@ -316,8 +319,8 @@ __device__ __forceinline__ void qk_first(f32x16_t& d, const u32x4_t& k, const u3
 __device__ __forceinline__ void qk_acc(f32x16_t& d, const u32x4_t& k, const u32x4_t& q) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "a"(q));
 }
-// The same with the 3 wait states that a VALU write of an operand just before needs: code
-// outside the steady-state loop, where the compiler may move operands between registers.
+// The same with the 3 wait states that a VALU write of an operand just before needs (the
+// first tile's QK, before the loop: the compiler may move the queries between registers).
 __device__ __forceinline__ void qk_first_s(f32x16_t& d, const u32x4_t& k, const u32x4_t& q) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(k), "a"(q));
 }
@@ -581,22 +584,17 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_pipe_kernel(PrefillAttnAr
     // the softmax reads S next: the wait states after the last MFMA
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 1" : "+v"(sA[0]), "+v"(sA[1]));
   }
-  // (hn: std::true_type when a tile t + 1 exists; hs: std::true_type outside the
-  // steady-state loop, where every MFMA takes the leading wait states)
-  auto step = [&](auto hn, auto hs, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) __attribute__((always_inline)) {
-    constexpr bool kNext = decltype(hn)::value, kSafe = decltype(hs)::value;
-    if constexpr (kNext) {
-      if (t + 2 < ntiles) pwait_vm<kDmaPerWave>();
-      else pwait_vm<0>();
-      pbarrier();
-      if (t + 3 < ntiles) issue(t + 3);
-    }
+  auto step = [&](int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) __attribute__((always_inline)) {
+    if (t + 2 < ntiles) pwait_vm<kDmaPerWave>();
+    else pwait_vm<0>();
+    pbarrier();
+    if (t + 3 < ntiles) issue(t + 3);
     if (t * kPT + kPT > unmasked) mask(t, sc);  // (uniform) on the diagonal or past Sk
     Soft z;
     u32x4_t vf[8];
     // phase 1: the QK of tile t + 1 with the softmax of sub-block 0 and the reference of
     // sub-block 1 (micro steps 0..17), the V^T reads of tile t in the last 8 slots
-    if constexpr (kNext) {
+    {
       u32x4_t kf[12];  // read two fragments ahead of their MFMAs
       kf[0] = kread(t + 1, 0);
       kf[1] = kread(t + 1, 1);
@@ -605,23 +603,14 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_pipe_kernel(PrefillAttnAr
         constexpr int i = decltype(ic)::value, ks = i >> 1, j = i & 1;
         if constexpr (j == 0 && ks + 2 < 12) kf[ks + 2] = kread(t + 1, ks + 2);
         if constexpr (i >= 16) vf[i - 16] = vread(t, i - 16);
-        if constexpr (kSafe) {
-          if constexpr (ks == 0) qk_first_s(sn[j], kf[0], qf[j][0]);
-          else qk_acc_s(sn[j], kf[ks], qf[j][ks]);
-        } else {
-          if constexpr (ks == 0) qk_first(sn[j], kf[0], qf[j][0]);
-          else qk_acc(sn[j], kf[ks], qf[j][ks]);
-        }
+        if constexpr (ks == 0) qk_first(sn[j], kf[0], qf[j][0]);
+        else qk_acc(sn[j], kf[ks], qf[j][ks]);
         constexpr int lo = i * 18 / 24, hi = (i + 1) * 18 / 24;
         pstatic_for<hi - lo>([&](auto kc) __attribute__((always_inline)) {
           micro(std::integral_constant<int, lo + decltype(kc)::value>{}, sc, z);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vf[i] = vread(t, i);
-      pstatic_for<18>([&](auto kc) __attribute__((always_inline)) { micro(kc, sc, z); });
     }
     // P of sub-block 0 and both factors are complete here (not sunk past the branch)
     asm volatile("" ::"v"(z.pb[0][0]), "v"(z.pb[0][1]), "v"(lsum[0]), "v"(z.mu[1]), "v"(z.ls[1]));
@@ -631,8 +620,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_pipe_kernel(PrefillAttnAr
     __builtin_amdgcn_sched_barrier(0);
     pstatic_for<8>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value, ss = i >> 2, vb = i & 3;
-      if constexpr (kSafe) pv_mfma(o[0][vb], vf[2 * vb + ss], z.pb[0][ss]);
-      else pv_mfma_nw(o[0][vb], vf[2 * vb + ss], z.pb[0][ss]);
+      pv_mfma_nw(o[0][vb], vf[2 * vb + ss], z.pb[0][ss]);
       micro(std::integral_constant<int, 18 + i>{}, sc, z);
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -640,22 +628,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_pipe_kernel(PrefillAttnAr
     for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb) {
-        if (kSafe || (ss == 0 && vb == 0)) pv_mfma(o[1][vb], vf[2 * vb + ss], z.pb[1][ss]);  // P just written
+        if (ss == 0 && vb == 0) pv_mfma(o[1][vb], vf[2 * vb + ss], z.pb[1][ss]);  // P just written
         else pv_mfma_nw(o[1][vb], vf[2 * vb + ss], z.pb[1][ss]);
       }
-    if constexpr (!kNext) {  // the wait states before anything reads or moves O
-      pv_drain(o[0]);
-      pv_drain(o[1]);
-    }
   };
   // Every step is the steady-state one: the last tile's step also runs a QK, of a tile
   // that does not exist (stale LDS into S registers nobody reads; 24 MFMAs per workgroup),
   // so the loop is the only copy of the step and needs no separately scheduled tail.
-  const std::true_type yes;
-  const std::false_type no;
   for (int t = 0; t < ntiles; t += 2) {
-    step(yes, no, t, sA, sB);
-    if (t + 1 < ntiles) step(yes, no, t + 1, sB, sA);
+    step(t, sA, sB);
+    if (t + 1 < ntiles) step(t + 1, sB, sA);
   }
   pv_drain(o[0]);  // the wait states before anything reads or moves O
   pv_drain(o[1]);
@@ -666,7 +648,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_pipe_kernel(PrefillAttnAr
   // rather than 16 bytes into each of 32 rows (partial lines, written back about three
   // times over).  Wave w uses an 8.5 KB region of stage (ntiles + w / 2) % 4: no DMA is in
   // flight any more, and every wave has passed the barrier after which that stage (tile
-  // ntiles - 3 or ntiles - 2, or one never filled) is read by nobody.
+  // ntiles - 4 or ntiles - 3, or one never filled) is read by nobody but the unused QK of
+  // the last step.
   constexpr int kEpRow = 68;  // floats per staged row (64 + 4 pad: b128 accesses free of conflicts)
   float* ep = (float*)(sm + ((ntiles + (w >> 1)) % kNStg) * kStg) + (w & 1) * (32 * kEpRow);
   float* epf = (float*)(sm + ((ntiles + (w >> 1)) % kNStg) * kStg) + 2 * 32 * kEpRow + (w & 1) * 32;
