@@ -336,11 +336,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
   const int lane = tid & 63, r32 = lane & 31, h2 = lane >> 5;
 
-  // Workgroups are dealt round-robin to the 8 XCDs; keep the head groups of
-  // one part on one XCD so that they share its L2 for the part's keys.
+  // Workgroups are dealt round-robin to the 8 XCDs.  XCD x takes a contiguous range of
+  // ceil(parts / 8) parts, so the parts of one request (consecutive in the plan) mostly
+  // share an XCD's L2 for their queries, and the head groups of one part share it for
+  // the part's keys.
   const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
   const int hg = slot % a.head_groups;
-  const int part = xcd + 8 * (slot / a.head_groups);
+  const int part = xcd * ((a.num_parts + 7) / 8) + slot / a.head_groups;
   if (part >= a.num_parts) return;
 
   const int R = a.Sq * a.N;
