@@ -10,12 +10,15 @@
 // to +-448, code = e4m3fn(y) (v_cvt_pk_fp8_f32, ties to even); w_scale = fp32(1 / s).
 //
 // GEMM: C[h][m][n] = w_scale * sum_g d[h][m][g] * sum_{k in g} A8[h][m][k] W8[h][n][k].
-// One workgroup (4 waves) per (128 n, BM m, head), K in chunks of 128 = one activation
-// group: the chunk's A rows are quantised on their way into LDS (amax over the 16 lanes
-// that hold a row, s = 448 / amax, codes of clamp(a * s)), the W rows are copied, and
-// each wave runs v_mfma_f32_32x32x64_f8f6f4 over its 32 n rows against the BM m columns
-// into a chunk accumulator that is added to the total scaled by that row's d = 1 / s
-// (the MFMA computes the tile transposed, so m is the lane column and d a lane scalar).
+// One workgroup (4 waves) per (128 n, BM m, head), the tiles of one head on one XCD (they
+// share its weights and activations in that XCD's L2), K in chunks of 128 = one activation
+// group, held in registers two chunks ahead when K > 128.  Per chunk: each row's max |a| (the 16
+// lanes that hold the row, reduced over their DPP row), then s = 448 / amax and
+// d = 1 / s by one thread per row, then the codes of clamp(a * s) into LDS beside the
+// copied W rows; each wave runs v_mfma_f32_32x32x64_f8f6f4 over its 32 n rows against
+// the BM m columns into a chunk accumulator that is added to the total scaled by that
+// row's d (the MFMA computes the tile transposed, so m is the lane column and d a lane
+// scalar).
 #include "common.h"
 #include "kernels.h"
 
@@ -88,16 +91,30 @@ __global__ __launch_bounds__(1024) void quant_weight_kernel(const uint16_t* W, i
   if (threadIdx.x == 0) *w_scale = 1.f / s;
 }
 
-template <int BM>
+// Maximum of a 32-bit lane value over the 16 lanes of its DPP row (lanes 16r..16r+15):
+// quad swaps (xor 1, xor 2), then the half-row and row mirrors pair each quad with the
+// others.
+__device__ __forceinline__ uint32_t row16_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
+  return x;
+}
+
+template <int BM, bool DB>
 __global__ __launch_bounds__(256) void bmm8_kernel(Bmm8Args g) {
   constexpr int MB = BM / 32;
   constexpr int AL = BM * 16 / 256;  // A chunks of 8 bf16 per thread and K chunk
   __shared__ __attribute__((aligned(16))) uint8_t sa[BM * kRow8];
   __shared__ __attribute__((aligned(16))) uint8_t sb[128 * kRow8];
-  __shared__ float sd[BM];
+  __shared__ uint32_t ss[BM];  // per row of the chunk: max |a| (bf16 bits), then s (fp32 bits)
+  __shared__ float sd[BM];     // per row of the chunk: d = 1 / s
   __shared__ __attribute__((aligned(16))) uint8_t sc[BM * 256];  // bf16 output tile [BM][128]
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l32 = l & 31, hh = l >> 5;
-  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * BM, h = blockIdx.z;
+  HeadTile ht;
+  if (!head_tile((g.Nn + 127) / 128, (g.M + BM - 1) / BM, g.H, &ht)) return;
+  const int n0 = ht.nb * 128, m0 = ht.mb * BM, h = ht.h;
   const uint16_t* A = g.A + (int64_t)h * g.a_sh;
   const uint8_t* B = g.B + (int64_t)h * g.b_sh;
   f32x16_t acc[MB];
@@ -106,53 +123,71 @@ __global__ __launch_bounds__(256) void bmm8_kernel(Bmm8Args g) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
 
-  // global -> registers for one K chunk (the next chunk's loads are in flight during the
-  // current chunk's MFMAs)
-  u32x4_t ra[AL], rb[4];
-  auto load = [&](int k0) __attribute__((always_inline)) {
+  // global -> registers for one K chunk; two register sets, so the loads of chunk k+2
+  // are in flight while chunks k and k+1 are quantised and multiplied
+  struct Chunk {
+    u32x4_t a[AL], b[4];
+  };
+  auto load = [&](Chunk& r, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int u = tid + 256 * i, m = u >> 4, c = u & 15;
-      ra[i] = u32x4_t{0, 0, 0, 0};
-      if (m0 + m < g.M) ra[i] = *(const u32x4_t*)(A + (int64_t)(m0 + m) * g.a_sm + k0 + 8 * c);
+      r.a[i] = u32x4_t{0, 0, 0, 0};
+      if (m0 + m < g.M) r.a[i] = *(const u32x4_t*)(A + (int64_t)(m0 + m) * g.a_sm + k0 + 8 * c);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = tid + 256 * i, n = u >> 3, c = u & 7;
-      rb[i] = u32x4_t{0, 0, 0, 0};
-      if (n0 + n < g.Nn) rb[i] = *(const u32x4_t*)(B + (int64_t)(n0 + n) * g.b_sn + k0 + 16 * c);
+      r.b[i] = u32x4_t{0, 0, 0, 0};
+      if (n0 + n < g.Nn) r.b[i] = *(const u32x4_t*)(B + (int64_t)(n0 + n) * g.b_sn + k0 + 16 * c);
     }
   };
-  load(0);
-  for (int k0 = 0; k0 < g.K; k0 += 128) {
-    // A: row m held by 16 consecutive lanes (8 values each): quantise the row's group
+  // One K chunk = one activation group per row.  Row m of A is held by the 16 lanes
+  // u = 16m .. 16m + 15 (one DPP row), 8 values each.
+  auto chunk = [&](Chunk& r, int k_next) __attribute__((always_inline)) {
+    // the group's max |a| per row: |bf16| compared as 15-bit integers (same order as the
+    // values), over the lane's 8 values, then over the row's 16 lanes
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int u = tid + 256 * i, m = u >> 4, c = u & 15;
-      float y[8];
-      float mx = 0.f;
+      uint32_t hi = 0, lo = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        y[2 * k] = bf16_to_f32((uint16_t)(ra[i][k] & 0xFFFF));
-        y[2 * k + 1] = bf16_to_f32((uint16_t)(ra[i][k] >> 16));
-        mx = fmaxf(mx, fmaxf(fabsf(y[2 * k]), fabsf(y[2 * k + 1])));
+        hi = max(hi, r.a[i][k] & 0x7FFF0000u);
+        lo = max(lo, r.a[i][k] & 0x7FFFu);
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const float s = 448.f / fmaxf(mx, 1e-10f);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = fminf(fmaxf(y[k] * s, -448.f), 448.f);
-      *(u32x2_t*)(sa + m * kRow8 + 8 * c) = to_fp8x8(y);
-      if (c == 0) sd[m] = 1.f / s;
+      const uint32_t mx = row16_max(max(hi >> 16, lo));
+      if (c == 0) ss[m] = mx;
     }
     // W: 128 rows x 8 chunks of 16 bytes
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = tid + 256 * i, n = u >> 3, c = u & 7;
-      *(u32x4_t*)(sb + n * kRow8 + 16 * c) = rb[i];
+      *(u32x4_t*)(sb + n * kRow8 + 16 * c) = r.b[i];
     }
     __syncthreads();
-    if (k0 + 128 < g.K) load(k0 + 128);
+    // s = 448 / max(amax, 1e-10) and d = 1 / s, both rounded to fp32, once per row
+    if (tid < BM) {
+      const float s = 448.f / fmaxf(bf16_to_f32((uint16_t)ss[tid]), 1e-10f);
+      sd[tid] = 1.f / s;
+      ss[tid] = __float_as_uint(s);
+    }
+    __syncthreads();
+    // codes of clamp(a * s, +-448) into the A tile
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int u = tid + 256 * i, m = u >> 4, c = u & 15;
+      const float s = __uint_as_float(ss[m]);
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y[2 * k] = fminf(fmaxf(__uint_as_float(r.a[i][k] << 16) * s, -448.f), 448.f);
+        y[2 * k + 1] = fminf(fmaxf(__uint_as_float(r.a[i][k] & 0xFFFF0000u) * s, -448.f), 448.f);
+      }
+      *(u32x2_t*)(sa + m * kRow8 + 8 * c) = to_fp8x8(y);
+    }
+    __syncthreads();
+    if (k_next < g.K) load(r, k_next);
     // operand bytes of lane l: row l % 32, k = 64 ks + 32 (l / 32) .. +31, the same order
     // for both operands (the MFMA pairs equal byte positions of the two lane halves)
     i32x8_t wa[2];
@@ -181,6 +216,19 @@ __global__ __launch_bounds__(256) void bmm8_kernel(Bmm8Args g) {
       for (int v = 0; v < 16; ++v) acc[mb][v] += part[v] * d;
     }
     __syncthreads();
+  };
+  if constexpr (DB) {
+    Chunk r0, r1;
+    load(r0, 0);
+    if (128 < g.K) load(r1, 128);
+    for (int k0 = 0; k0 < g.K; k0 += 256) {
+      chunk(r0, k0 + 256);
+      if (k0 + 128 < g.K) chunk(r1, k0 + 384);
+    }
+  } else {  // one register set (K = 128: a single chunk), fewer registers per wave
+    Chunk r0;
+    load(r0, 0);
+    for (int k0 = 0; k0 < g.K; k0 += 128) chunk(r0, k0 + 128);
   }
   // Epilogue through LDS: each lane's 4 consecutive n of one m go to the tile as 8 bytes
   // (16-byte chunks of a 256-byte row XOR-swizzled by row), then rows leave as 16-byte
@@ -219,8 +267,16 @@ hipError_t launch_bmm8(const Bmm8Args& g, hipStream_t stream) {
   const int nb = (g.Nn + 127) / 128;
   // 128-row tiles unless that leaves fewer workgroups than the 256 compute units
   const bool big = (int64_t)nb * ((g.M + 127) / 128) * g.H >= 256;
-  if (big) hipLaunchKernelGGL(bmm8_kernel<128>, dim3(nb, (g.M + 127) / 128, g.H), dim3(256), 0, stream, g);
-  else hipLaunchKernelGGL(bmm8_kernel<64>, dim3(nb, (g.M + 63) / 64, g.H), dim3(256), 0, stream, g);
+  const bool db = g.K > 128;  // two register sets only where there is a next chunk
+  const int64_t tiles = (int64_t)nb * ((g.M + (big ? 127 : 63)) / (big ? 128 : 64)) * g.H;
+  const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)));
+  if (big) {
+    if (db) hipLaunchKernelGGL((bmm8_kernel<128, true>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((bmm8_kernel<128, false>), grid, dim3(256), 0, stream, g);
+  } else {
+    if (db) hipLaunchKernelGGL((bmm8_kernel<64, true>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((bmm8_kernel<64, false>), grid, dim3(256), 0, stream, g);
+  }
   return hipGetLastError();
 }
 

@@ -21,6 +21,25 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
 
 __device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 
+// Tiles of a per-head batched GEMM in a 1-D launch.  The dispatcher deals workgroups to
+// the 8 XCDs round-robin, so launch index L runs on XCD L % 8; XCD x takes the tiles
+// x * per_xcd .. (x + 1) * per_xcd - 1 in (head, m block, n block) order, so the tiles
+// that read one head's operands run on one XCD and share its L2.  The launch has
+// 8 * per_xcd workgroups, per_xcd = ceil(tiles / 8); false past the last tile.
+struct HeadTile {
+  int h, mb, nb;
+};
+__device__ __forceinline__ bool head_tile(int nbk, int mbk, int H, HeadTile* t) {
+  const int64_t tiles = (int64_t)nbk * mbk * H;
+  const int64_t per_xcd = (tiles + 7) / 8;
+  const int64_t item = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= tiles) return false;
+  t->nb = (int)(item % nbk);
+  t->mb = (int)((item / nbk) % mbk);
+  t->h = (int)(item / ((int64_t)nbk * mbk));
+  return true;
+}
+
 // Round-to-nearest-even float -> bf16 pattern (gfx950 converts in hardware).
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));

@@ -30,18 +30,22 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {  // [row][16 chunk
   return row * 256 + ((chunk ^ (row & 15)) << 4);
 }
 
-// One workgroup per (128 n, BM m, head): with M <= BM every weight element is read once
-// (BM = 64 when 128 would leave fewer workgroups than compute units).  K goes in chunks of
-// 128; the next chunk's global loads are issued into registers before the current chunk's
-// MFMAs, so the loads of chunk k+1 overlap the math of chunk k.
-template <bool B_NCONTIG, int BM>
+// One workgroup per (128 n, BM m, head), the tiles of one head on one XCD: with M <= BM
+// every weight element is read once (BM = 64 when 128 would leave fewer workgroups than
+// compute units; the two m blocks then share the head's weights in that XCD's L2).  K goes in chunks of
+// 128; with more than one chunk they go through two register sets: the global loads of
+// chunk k+2 are issued once chunk k is in LDS, so they overlap the math of chunk k and the
+// staging and math of chunk k+1.
+template <bool B_NCONTIG, int BM, bool DB>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   constexpr int MB = BM / 32;      // 32-row MFMA blocks of the tile's m
   constexpr int AL = BM * 16 / 256;  // A loads per thread and chunk
   __shared__ __attribute__((aligned(16))) char sa[BM * kBK * 2];
   __shared__ __attribute__((aligned(16))) char sb[kBN * kBK * 2];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l32 = l & 31, hh = l >> 5;
-  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * BM, h = blockIdx.z;
+  HeadTile ht;
+  if (!head_tile((g.Nn + kBN - 1) / kBN, (g.M + BM - 1) / BM, g.H, &ht)) return;
+  const int n0 = ht.nb * kBN, m0 = ht.mb * BM, h = ht.h;
   const uint16_t* A = g.A + (int64_t)h * g.a_sh;
   const uint16_t* B = g.B + (int64_t)h * g.b_sh;
   f32x16_t acc[MB];
@@ -50,43 +54,46 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
 
-  // global -> registers for one K chunk
-  u32x4_t ra[AL], rb[8];
-  auto load = [&](int k0) __attribute__((always_inline)) {
+  // global -> registers for one K chunk; two register sets, so the loads of chunk k+2
+  // are in flight while chunks k and k+1 are staged and multiplied
+  struct Chunk {
+    u32x4_t a[AL], b[8];
+  };
+  auto load = [&](Chunk& r, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {  // A: BM rows x 16 chunks
       const int u = tid + 256 * i, m = u >> 4, c = u & 15;
-      ra[i] = u32x4_t{0, 0, 0, 0};
-      if (m0 + m < g.M && k0 + 8 * c < g.K) ra[i] = *(const u32x4_t*)(A + (int64_t)(m0 + m) * g.a_sm + k0 + 8 * c);
+      r.a[i] = u32x4_t{0, 0, 0, 0};
+      if (m0 + m < g.M && k0 + 8 * c < g.K) r.a[i] = *(const u32x4_t*)(A + (int64_t)(m0 + m) * g.a_sm + k0 + 8 * c);
     }
     if constexpr (!B_NCONTIG) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {  // B: 128 rows (n) x 16 chunks (k)
         const int u = tid + 256 * i, n = u >> 4, c = u & 15;
-        rb[i] = u32x4_t{0, 0, 0, 0};
-        if (n0 + n < g.Nn && k0 + 8 * c < g.K) rb[i] = *(const u32x4_t*)(B + (int64_t)(n0 + n) * g.b_sn + k0 + 8 * c);
+        r.b[i] = u32x4_t{0, 0, 0, 0};
+        if (n0 + n < g.Nn && k0 + 8 * c < g.K) r.b[i] = *(const u32x4_t*)(B + (int64_t)(n0 + n) * g.b_sn + k0 + 8 * c);
       }
     } else {  // B: 8 rows (k) x 8 n per thread, transposed on the way to LDS
       const int ko = tid >> 4, no = tid & 15;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int k = k0 + 8 * ko + e;
-        rb[e] = u32x4_t{0, 0, 0, 0};
-        if (k < g.K && n0 + 8 * no < g.Nn) rb[e] = *(const u32x4_t*)(B + (int64_t)k * g.b_sk + n0 + 8 * no);
+        r.b[e] = u32x4_t{0, 0, 0, 0};
+        if (k < g.K && n0 + 8 * no < g.Nn) r.b[e] = *(const u32x4_t*)(B + (int64_t)k * g.b_sk + n0 + 8 * no);
       }
     }
   };
-  auto store = [&]() __attribute__((always_inline)) {
+  auto store = [&](const Chunk& r) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int u = tid + 256 * i;
-      *(u32x4_t*)(sa + tile_off(u >> 4, u & 15)) = ra[i];
+      *(u32x4_t*)(sa + tile_off(u >> 4, u & 15)) = r.a[i];
     }
     if constexpr (!B_NCONTIG) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int u = tid + 256 * i;
-        *(u32x4_t*)(sb + tile_off(u >> 4, u & 15)) = rb[i];
+        *(u32x4_t*)(sb + tile_off(u >> 4, u & 15)) = r.b[i];
       }
     } else {
       const int ko = tid >> 4, no = tid & 15;
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         u32x4_t o;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t x = rb[2 * k][c >> 1], y = rb[2 * k + 1][c >> 1];
+          const uint32_t x = r.b[2 * k][c >> 1], y = r.b[2 * k + 1][c >> 1];
           o[k] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
         }
         *(u32x4_t*)(sb + tile_off(8 * no + c, ko)) = o;
@@ -103,11 +110,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   };
 
-  load(0);
-  for (int k0 = 0; k0 < g.K; k0 += kBK) {
-    store();
+  auto chunk = [&](Chunk& r, int k_next) __attribute__((always_inline)) {
+    store(r);
     __syncthreads();
-    if (k0 + kBK < g.K) load(k0 + kBK);  // in flight during this chunk's MFMAs
+    if (k_next < g.K) load(r, k_next);  // in flight during this chunk's and the next one's work
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const u32x4_t af = *(const u32x4_t*)(sb + tile_off(32 * w + l32, 2 * ks + hh));
@@ -118,6 +124,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       }
     }
     __syncthreads();
+  };
+  if constexpr (DB) {
+    Chunk r0, r1;
+    load(r0, 0);
+    if (kBK < g.K) load(r1, kBK);
+    for (int k0 = 0; k0 < g.K; k0 += 2 * kBK) {
+      chunk(r0, k0 + 2 * kBK);
+      if (k0 + kBK < g.K) chunk(r1, k0 + 3 * kBK);
+    }
+  } else {  // one register set (K <= 128: a single chunk), fewer registers per wave
+    Chunk r0;
+    load(r0, 0);
+    for (int k0 = 0; k0 < g.K; k0 += kBK) chunk(r0, k0 + kBK);
   }
   // Epilogue through LDS (the B tile's space, free after the last barrier): each lane's
   // 4 consecutive n of one m go to the tile as 8 bytes; then rows leave as 16-byte pieces,
@@ -349,14 +368,25 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
   // 128-row tiles unless that leaves fewer workgroups than the 256 compute units
   const bool big = (int64_t)nb * ((g.M + 127) / 128) * g.H >= 256;
   const dim3 block(256);
+  const bool db = g.K > kBK;  // two register sets only where there is a next chunk
+  const int64_t tiles = (int64_t)nb * ((g.M + (big ? 127 : 63)) / (big ? 128 : 64)) * g.H;
+  const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)));
   if (big) {
-    const dim3 grid(nb, (g.M + 127) / 128, g.H);
-    if (g.b_sk == 1) hipLaunchKernelGGL((gemm_kernel<false, 128>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((gemm_kernel<true, 128>), grid, block, 0, stream, g);
+    if (g.b_sk == 1) {
+      if (db) hipLaunchKernelGGL((gemm_kernel<false, 128, true>), grid, block, 0, stream, g);
+      else hipLaunchKernelGGL((gemm_kernel<false, 128, false>), grid, block, 0, stream, g);
+    } else {
+      if (db) hipLaunchKernelGGL((gemm_kernel<true, 128, true>), grid, block, 0, stream, g);
+      else hipLaunchKernelGGL((gemm_kernel<true, 128, false>), grid, block, 0, stream, g);
+    }
   } else {
-    const dim3 grid(nb, (g.M + 63) / 64, g.H);
-    if (g.b_sk == 1) hipLaunchKernelGGL((gemm_kernel<false, 64>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((gemm_kernel<true, 64>), grid, block, 0, stream, g);
+    if (g.b_sk == 1) {
+      if (db) hipLaunchKernelGGL((gemm_kernel<false, 64, true>), grid, block, 0, stream, g);
+      else hipLaunchKernelGGL((gemm_kernel<false, 64, false>), grid, block, 0, stream, g);
+    } else {
+      if (db) hipLaunchKernelGGL((gemm_kernel<true, 64, true>), grid, block, 0, stream, g);
+      else hipLaunchKernelGGL((gemm_kernel<true, 64, false>), grid, block, 0, stream, g);
+    }
   }
   return hipGetLastError();
 }
