@@ -452,14 +452,27 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   // Widens chunk i of this wave's raw rows (slot `raw`, LDS address) into the bf16 stage
   // at byte offset `dst` of smem: i < 8 is row i, values 8 lane .. +7 (latent); i = 8 is
   // row lane / 8, rope values 8 (lane % 8) .. +7.
-  auto widen = [&](uint32_t raw, uint32_t dst, auto ic) __attribute__((always_inline)) {
+  // The read and the conversion are separate steps, so that inside the QK chain the read
+  // of chunk i+1 is issued a few MFMAs before its conversion (waiting for a read issued
+  // just before would drain the K fragment reads in flight as well; the generic-page form
+  // keeps the one-step widen, having no registers to spare).
+  auto widen_rd = [&](uint32_t raw, auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
     const int ln = i < 8 ? lane : lane_now();  // (i = 8: no lane offset kept live for it)
     const int row = i < 8 ? i : (ln >> 3);
     const int col8 = i < 8 ? ln : 64 + (ln & 7);
-    const u32x2_t v = *(const u32x2_t*)(smem + (raw - smem0) + row * kHead + 8 * col8);
+    return *(const u32x2_t*)(smem + (raw - smem0) + row * kHead + 8 * col8);
+  };
+  auto widen_wr = [&](uint32_t dst, auto ic, const u32x2_t& v) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    const int ln = i < 8 ? lane : lane_now();
+    const int row = i < 8 ? i : (ln >> 3);
+    const int col8 = i < 8 ? ln : 64 + (ln & 7);
     const u32x2_t lo = fp8x4_to_bf16x4(v[0]), hi = fp8x4_to_bf16x4(v[1]);
     *(u32x4_t*)(smem + dst + (8 * w + row) * kRowB + 16 * col8) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto widen = [&](uint32_t raw, uint32_t dst, auto ic) __attribute__((always_inline)) {
+    widen_wr(dst, ic, widen_rd(raw, ic));
   };
 
   // ---- fp8 queries: all waves load each raw tile into its slot of the 4-slot ring: wave
@@ -786,8 +799,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             static_for<DMA0>([&](auto nc) __attribute__((always_inline)) {
               if (dma_il) dma_one(dt, nc);
             });
+          u32x2_t wv[2];  // fp8: raw bytes of chunk i to widen in wv[i % 2], read one chunk ahead
           static_for<36>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
+            if constexpr (RAWW && FAST && k == 0) {
+              if (widen_next) wv[0] = widen_rd(raw_slot(g + 1), std::integral_constant<int, 0>{});
+            }
             if constexpr (QF8) {
               // (not reached: the fp8-query chain above)
             } else if constexpr (k == 0)
@@ -803,7 +820,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             }
             // fp8: widen this wave's rows of tile s+1, then load raw tile s+3 into their slot
             if constexpr (RAWW && k >= 2 && k % 3 == 2 && k / 3 < 9) {
-              if (widen_next) widen(raw_slot(g + 1), wst, std::integral_constant<int, k / 3>{});
+              if (widen_next) {
+                constexpr int i = k / 3;
+                if constexpr (FAST) {
+                  if constexpr (i + 1 < 9) wv[(i + 1) & 1] = widen_rd(raw_slot(g + 1), std::integral_constant<int, i + 1>{});
+                  widen_wr(wst, std::integral_constant<int, i>{}, wv[i & 1]);
+                } else {  // (generic pages: no registers to spare for the read-ahead)
+                  widen(raw_slot(g + 1), wst, std::integral_constant<int, i>{});
+                }
+              }
             }
             if constexpr (RAWW && k == 30) {
               if (do_dma) dma_raw(dt);
