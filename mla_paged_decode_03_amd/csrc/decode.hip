@@ -83,6 +83,16 @@ __device__ __forceinline__ void wait_tiles(int newer) {
     default: wait_vm<3 * PER>(); break;
   }
 }
+// The same wait in the step loop, where `newer` is 1 but for a segment's first steps and
+// a part's last ones: with newer >= 1 it leaves MIN (the fewest DMA instructions any wave
+// issues per tile) loads outstanding, which waits for at least the awaited tile, and the
+// branch stays two adjacent blocks (a switch laid out away from the loop cost each step
+// a few hundred cycles of jumps there and back).
+template <int MIN>
+__device__ __forceinline__ void wait_landed(int newer) {
+  if (newer > 0) wait_vm<MIN>();
+  else wait_vm<0>();
+}
 // Workgroup barrier that also orders this wave's LDS accesses (and does not drain vmcnt).
 // The lgkmcnt(0) wait is the compiler's own, so it knows that every LDS and scalar load
 // issued before is complete and places no conservative waits after the barrier.
@@ -700,10 +710,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
       // then loads the next raw tile into the slot that frees
       const bool widen_next = RAWW && widened == g + 1 && widened < issued;  // wave-uniform
       if constexpr (QF8) {
-        if (!last) {  // this wave's part of tile s has landed
-          if (w == 3) wait_tiles<4>(issued - g - 1);
-          else wait_tiles<5>(issued - g - 1);
-        }
+        if (!last) wait_landed<4>(issued - g - 1);  // this wave's part of tile s has landed
         // raw slot of tile g-1 is free after this barrier: tiles up to g+3 may be in flight
         do_dma = pf.si < s_end && issued < g + kQSlots;
         if (do_dma) dt = dma_tile<true, FAST>(a, pf, smem0 + ((unsigned)issued % kQSlots) * kQSlotB);
@@ -711,10 +718,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
         do_dma = pf.si < s_end && issued < widened + (widen_next ? 3 : 2);
         if (do_dma) dt = dma_tile<true, FAST>(a, pf, raw_slot(issued));
       } else {
-        if (!last) {  // this wave's part of tile s has landed
-          if (w0) wait_tiles<10>(issued - g - 1);
-          else wait_tiles<9>(issued - g - 1);
-        }
+        if (!last) wait_landed<9>(issued - g - 1);  // this wave's part of tile s has landed
         // a stage is free once the P.V of its tile is complete: before this barrier, every
         // tile up to g-2 (g-1 at the segment's first step)
         do_dma = pf.si < s_end && issued < g + (first ? kStages : kStages - 1);
