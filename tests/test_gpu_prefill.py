@@ -50,6 +50,11 @@ def _check(o, lse, ro, rl, where=""):
     # unmasked launches run the pipelined kernel: odd and even tile counts (3, 5, 32)
     # through its loop and tail steps, query blocks of 256 with ragged ends
     (False, [300, 513, 257], [70, 160, 1000]),
+    # causal launches pair query blocks (nqb - 1 - p, p) per workgroup: an odd block
+    # count (5: the middle block alone), an even one (4), requests whose high block of a
+    # pair is empty, keys beyond the queries (context), and an empty request
+    (True, [600, 1100, 257, 0, 900], [700, 1100, 300, 4, 1500]),
+    (True, [1024, 513], [1024, 600]),
 ])
 def test_prefill_attention(torch_cuda, causal, sq, sk):
     torch = torch_cuda
