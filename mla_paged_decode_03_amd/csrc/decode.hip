@@ -461,11 +461,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   };
   // Widens chunk i of this wave's raw rows (slot `raw`, LDS address) into the bf16 stage
   // at byte offset `dst` of smem: i < 8 is row i, values 8 lane .. +7 (latent); i = 8 is
-  // row lane / 8, rope values 8 (lane % 8) .. +7.
-  // The read and the conversion are separate steps, so that inside the QK chain the read
-  // of chunk i+1 is issued a few MFMAs before its conversion (waiting for a read issued
-  // just before would drain the K fragment reads in flight as well; the generic-page form
-  // keeps the one-step widen, having no registers to spare).
+  // row lane / 8, rope values 8 (lane % 8) .. +7.  Read and conversion are separate
+  // steps, so that all 9 reads of a tile can be in flight at once.
   auto widen_rd = [&](uint32_t raw, auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
     const int ln = i < 8 ? lane : lane_now();  // (i = 8: no lane offset kept live for it)
@@ -483,6 +480,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
   };
   auto widen = [&](uint32_t raw, uint32_t dst, auto ic) __attribute__((always_inline)) {
     widen_wr(dst, ic, widen_rd(raw, ic));
+  };
+  // The whole tile: the 9 reads issued together, then the conversions and writes, each
+  // after its own read (the compiler pairs the reads and waits for them in order).
+  auto widen_all = [&](uint32_t raw, uint32_t dst) __attribute__((always_inline)) {
+    u32x2_t v[9];
+    static_for<9>([&](auto ic) __attribute__((always_inline)) { v[decltype(ic)::value] = widen_rd(raw, ic); });
+    static_for<9>([&](auto ic) __attribute__((always_inline)) { widen_wr(dst, ic, v[decltype(ic)::value]); });
   };
 
   // ---- fp8 queries: all waves load each raw tile into its slot of the 4-slot ring: wave
@@ -759,7 +763,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
         // (then it is issued here, with the clamped offsets)
         const bool dma_il = !FP8 && do_dma && (!FAST || dt.kmax >= wkey);  // wave-uniform
         if (!FP8 && !last && do_dma && !dma_il) dma_all(dt);
-        if (RAWW && !last && widen_next) raw_ready();
+        // fp8 (pages of 32 keys): this wave's rows of tile s+1 widened at once, before the
+        // QK chain (spread between its MFMAs, the widening's LDS writes stall the K reads
+        // longer than the whole widening takes here)
+        if (RAWW && !last && widen_next) {
+          raw_ready();
+          if constexpr (FAST) widen_all(raw_slot(g + 1), wst);
+        }
         if (QF8 && !last && do_dma) dma_q8(dt);
         // ---- fp8 queries: S^T = K . Q^T in 9 fp8 k-steps of 64 dims over the raw tile,
         // with this wave's rows of the tile's value columns widened between them ----
@@ -803,12 +813,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             static_for<DMA0>([&](auto nc) __attribute__((always_inline)) {
               if (dma_il) dma_one(dt, nc);
             });
-          u32x2_t wv[2];  // fp8: raw bytes of chunk i to widen in wv[i % 2], read one chunk ahead
           static_for<36>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
-            if constexpr (RAWW && FAST && k == 0) {
-              if (widen_next) wv[0] = widen_rd(raw_slot(g + 1), std::integral_constant<int, 0>{});
-            }
             if constexpr (QF8) {
               // (not reached: the fp8-query chain above)
             } else if constexpr (k == 0)
@@ -822,18 +828,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeArgs a) {
             if constexpr (!FP8 && k % 3 == 2 && n < 10) {
               if (dma_il) dma_one(dt, std::integral_constant<int, n>{});
             }
-            // fp8: widen this wave's rows of tile s+1, then load raw tile s+3 into their slot
-            if constexpr (RAWW && k >= 2 && k % 3 == 2 && k / 3 < 9) {
-              if (widen_next) {
-                constexpr int i = k / 3;
-                if constexpr (FAST) {
-                  if constexpr (i + 1 < 9) wv[(i + 1) & 1] = widen_rd(raw_slot(g + 1), std::integral_constant<int, i + 1>{});
-                  widen_wr(wst, std::integral_constant<int, i>{}, wv[i & 1]);
-                } else {  // (generic pages: no registers to spare for the read-ahead)
-                  widen(raw_slot(g + 1), wst, std::integral_constant<int, i>{});
-                }
-              }
+            // fp8, generic pages: widen this wave's rows of tile s+1 between the MFMAs
+            if constexpr (RAWW && !FAST && k >= 2 && k % 3 == 2 && k / 3 < 9) {
+              if (widen_next) widen(raw_slot(g + 1), wst, std::integral_constant<int, k / 3>{});
             }
+            // fp8: load raw tile s+3 into the slot the widening freed
             if constexpr (RAWW && k == 30) {
               if (do_dma) dma_raw(dt);
             }
