@@ -394,6 +394,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--settle-ms", type=float, default=60.0,
                     help="GPU milliseconds of untimed steps before the warmup (clock ramp after idle)")
+    ap.add_argument("--ramp", type=int, default=0,
+                    help="instead of the bench line: after 1 s of idle, the GPU time per step of N steps in "
+                         "blocks of 10 (the clock ramp the settle phase skips)")
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -514,6 +517,19 @@ def main():
         if w.absorb:
             up()
 
+    if args.ramp > 0:
+        torch.cuda.synchronize()
+        time.sleep(1.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.ramp // 10 + 1)]
+        ev[0].record()
+        for i in range(args.ramp // 10 * 10):
+            step()
+            if (i + 1) % 10 == 0:
+                ev[(i + 1) // 10].record()
+        torch.cuda.synchronize()
+        us = [round(ev[j].elapsed_time(ev[j + 1]) / 10 * 1e3, 1) for j in range(len(ev) - 1)]
+        print(json.dumps({"workload": w.name, "ramp_us_per_step_blocks_of_10": us}))
+        return
     settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
