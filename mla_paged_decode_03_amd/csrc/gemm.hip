@@ -350,13 +350,16 @@ __global__ __launch_bounds__(256, 1) void kvb_gemm_kernel(KvbArgs g) {
                     pack_bf16x2(acc[nb][sb][4 * gq + 2], acc[nb][sb][4 * gq + 3])};
       }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (lgkmcnt(0))
+  // Non-temporal stores: the 256 MB-scale outputs stream past L2 (measured on the chunked
+  // prefill step: 6.90-6.99 -> 6.69-6.74 ms, the GEMM's own time unchanged; the gain is in
+  // the attention launches that follow it).
 #pragma unroll
   for (int it = 0; it < 32; ++it) {
     const int u = lane + 64 * it, r = u >> 4, c = u & 15;  // (r >> 4) & 1 == (it >> 2) & 1
     const int s = s0 + 128 * ws + r, n = n0 + 128 * wn + 8 * c;
     u32x4_t val = *(const u32x4_t*)(ot + r * 256 + ((c ^ (r & 15)) << 4));
     if ((it >> 2) & 1) val = u32x4_t{val[2], val[3], val[0], val[1]};
-    if (s < g.M && n < Nn) *(u32x4_t*)(C + (int64_t)s * Nn + n) = val;
+    if (s < g.M && n < Nn) __builtin_nontemporal_store(val, (u32x4_t*)(C + (int64_t)s * Nn + n));
   }
 }
 
