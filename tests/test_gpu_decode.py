@@ -127,6 +127,9 @@ CASES = [
     (128, 1, 64, [300, 1000], "fp8", 0),
     (16, 1, 64, [4000, 100], "fp8", 6),
     (128, 4, 64, [257, 2], "fp8", 3),
+    (128, 1, 16, [300, 1000], "fp8", 0),            # fp8, generic pages (16 keys)
+    (16, 2, 7, [90, 13], "fp8", 3),                 # fp8, odd page size, split
+    (32, 1, 1, [5, 70], "fp8", 2),                  # fp8, page size 1
 ]
 
 
@@ -376,3 +379,38 @@ def test_gather_addressing_dominant_keys(torch_cuda, ps, L, cus):
         assert np.array_equal(o[0, h], bf16_to_f64(flat[r, :512])), (h, js[h], r)
     ro, _ = oracle(inp)
     assert np.max(np.abs(o - ro)) <= 1e-6  # the fp64 oracle agrees (all weight on one key)
+
+
+@pytest.mark.parametrize("dt,ps", [("bf16", 64), ("fp8", 64), ("bf16", 16), ("fp8", 16)])
+def test_rope_in_its_own_buffer(torch_cuda, dt, ps):
+    """The cache's rope columns given through their own base pointer (cache_k_pe, same
+    strides as the latent rows), as a cache split into kv_c and k_pe allocations is: the
+    rope columns of the main buffer are poisoned (NaN for bf16, 0x7F = NaN for e4m3) and
+    must not be read."""
+    api = _api()
+    torch = torch_cuda
+    name = "fp8" if dt == "fp8" else "tiny"
+    inp = gen_case(name, seq_lens=np.array([700, 45, 300], np.int32), B=3, N=128, Sq=1, page_size=ps,
+                   pool_pages=None, seed=91)
+    w = inp.w
+    if dt == "bf16":
+        cache = bf16_dev(inp.cache)
+        poison = torch.full_like(cache[..., 512:], float("nan"))
+    else:
+        cache = u8_dev(inp.cache)
+        poison = torch.full_like(cache[..., 512:], 0x7F)
+    pe = torch.zeros_like(cache)  # same shape and strides; only its first 64 columns are rope
+    pe[..., :64] = cache[..., 512:]
+    cache[..., 512:] = poison
+    q, q_pe = bf16_dev(inp.q), bf16_dev(inp.q_pe)
+    bt = torch.from_numpy(inp.block_table).to("cuda")
+    sl = torch.from_numpy(inp.seq_lens).to("cuda")
+    o = torch.full((w.T, w.N, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((w.T, w.N), float("nan"), dtype=torch.float32, device="cuda")
+    kd = api.MLA_DT_BF16 if dt == "bf16" else api.MLA_DT_FP8_E4M3FN
+    plan = api.mla_decode_plan(inp.seq_lens, w.Sq, w.N, ps, inp.block_table.shape[1], kd, 0)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    api.mla_decode_run(plan, q, q_pe, cache, bt, sl, w.scale, inp.kv_scale, o, lse, ws, cache_k_pe=pe)
+    torch.cuda.synchronize()
+    ro, rl = oracle(inp)
+    check(bf16_host(o), lse.cpu().numpy().astype(np.float64), ro, rl)
