@@ -414,3 +414,18 @@ def test_rope_in_its_own_buffer(torch_cuda, dt, ps):
     torch.cuda.synchronize()
     ro, rl = oracle(inp)
     check(bf16_host(o), lse.cpu().numpy().astype(np.float64), ro, rl)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_one_long_request_split_over_the_chip(torch_cuda, dt):
+    """One request of 200,003 keys (ragged last page and tile) with 16 heads: the plan cuts
+    it into one segment per compute unit, so the reduce merges a few hundred partial states
+    per row (beyond the first batch of partial loads it issues together)."""
+    name = "fp8" if dt == "fp8" else "tiny"
+    inp = gen_case(name, seq_lens=np.array([200003], np.int32), B=1, N=16, Sq=1, page_size=64,
+                   pool_pages=None, seed=23)
+    o, lse, plan = run_decode(torch_cuda, inp, num_cus=0)
+    work, red = _api().mla_plan_export(plan)
+    assert len(work) >= 200 and len(red) == 1
+    ro, rl = oracle(inp)
+    check(o, lse, ro, rl)
